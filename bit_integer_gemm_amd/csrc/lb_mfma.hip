@@ -1,0 +1,313 @@
+// lb_mfma.hip -- int8 / int4 GEMM and the int8 linear layer on gfx950 int8 MFMA.
+//
+// What is computed: C = A x B with exact int32 accumulation for 8-bit and
+// 4-bit operands (digest of "Leveraging Large-Scale Data for Efficient Low-Bit
+// CUTLASS GEMM Optimization via Neural Networks": editor's summary for the bit
+// widths, Research results item 1 for the tiled product), and the linear layer
+// of Research results item 4 with a per-row x per-column fp32 dequantisation
+// fused into the store.
+//
+// How (MI355X-first; the pages' CUTLASS/Tensor-Core design is prior art):
+//  * One workgroup per BM x BN tile of C, NW waves in a WM x WN grid; each wave
+//    owns a (BM/WM) x (BN/WN) sub-tile held in int32 accumulators.
+//  * K is walked in stages of BK bytes.  A stage is an LDS buffer holding the
+//    A and B slices as 1 KiB "fragment blocks": 16 rows x 64 K-bytes, stored in
+//    the order the MFMA consumes them (lane i's 16 bytes at offset 16*i, lane i
+//    covering row i%16 and K-bytes 16*(i/16)..+15).  A copy instruction fills
+//    exactly one block, so LDS reads are 1 KiB contiguous per wave (no bank
+//    conflicts) and each lane's global read is a 16-byte piece of a 64-byte
+//    row segment.
+//  * ST stages (2, 3 or 4) form a ring filled by direct global->LDS copies
+//    issued ST-1 stages ahead (the multi-stage pipeline of Research results
+//    item 1; the 2-stage case is classic double buffering).
+//  * v_mfma_i32_16x16x64_i8 with the B fragment as the first source and the A
+//    fragment as the second: the 4 accumulators of lane i then hold
+//    C[m = i%16][n = 4*(i/16) .. +3], four consecutive columns, so the store is
+//    one 16-byte write per lane.  Any permutation of K shared by A and B leaves
+//    the product unchanged, so the MFMA's internal K order need not match
+//    memory order.
+//  * int4: the LDS holds packed bytes.  After the LDS read each 32-bit word w
+//    becomes lo = (w << 4) & 0xF0F0F0F0 (even k) and hi = w & 0xF0F0F0F0 (odd
+//    k): every nibble moves to the top of its own byte, i.e. the int8 value
+//    16*v with v's sign bit as the byte's sign bit.  MFMA then sums 256*a*b
+//    exactly and an arithmetic shift by 8 recovers C.
+//  * Rows past M or N read as zero through the buffer range check; a partial
+//    last K stage has its out-of-range A pieces zeroed in LDS before use.
+#include "lb_device.hpp"
+#include "lb_internal.hpp"
+
+namespace lb {
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int ST_>
+struct MfmaCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, ST = ST_;
+    static constexpr int NW = WM * WN, NT = NW * 64;
+    static constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
+    static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 fragments per wave
+    static constexpr int KB = BK / 64;                // 64-byte K blocks per stage
+    static constexpr int ABLK = (BM / 16) * KB, BBLK = (BN / 16) * KB;
+    static constexpr int NDMA_A = ABLK / NW, NDMA_B = BBLK / NW, NDMA = NDMA_A + NDMA_B;
+    static constexpr int STAGE_BYTES = (ABLK + BBLK) * 1024;
+    static_assert(BK % 64 == 0 && TM % 16 == 0 && TN % 16 == 0, "tile shape");
+    static_assert(ABLK % NW == 0 && BBLK % NW == 0, "copies must split evenly over waves");
+    static_assert(NDMA * (ST - 2) < 64, "vmcnt range");
+    static_assert(ST * STAGE_BYTES <= 160 * 1024, "LDS");
+};
+
+// Out-of-range K pieces of A in the last (partial) stage are zeroed in LDS:
+// with A's extra K at zero, whatever B holds there contributes nothing.
+template <class C>
+__device__ inline void zero_k_tail(char *stage, uint32_t lane, uint32_t wave,
+                                   int64_t k0, int64_t Kb)
+{
+#pragma unroll
+    for (int i = 0; i < C::NDMA_A; ++i) {
+        const int j = (int)wave + C::NW * i;
+        const int kb = j / (C::BM / 16);
+        const int64_t kbyte = k0 + kb * 64 + (int)(lane / 16) * 16;
+        if (kbyte >= Kb)
+            *(i32x4 *)(stage + j * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+    }
+}
+
+template <int N, int ST>
+__device__ inline void wait_outstanding(int tiles_after)
+{
+    // tiles_after = number of later stages already in flight (0..ST-2)
+    if constexpr (ST == 2) {
+        wait_vm_barrier<0>();
+    } else if constexpr (ST == 3) {
+        if (tiles_after >= 1) wait_vm_barrier<N>(); else wait_vm_barrier<0>();
+    } else {
+        if (tiles_after >= 2) wait_vm_barrier<2 * N>();
+        else if (tiles_after == 1) wait_vm_barrier<N>();
+        else wait_vm_barrier<0>();
+    }
+}
+
+__device__ inline i32x4 mfma16(i32x4 a, i32x4 b, i32x4 c)
+{
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+template <class C, int KIND>
+__global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
+    const int8_t *__restrict__ A, const int8_t *__restrict__ B, void *__restrict__ out,
+    const float *__restrict__ sx, const float *__restrict__ sw,
+    int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE_BYTES];
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wm = wave / C::WN, wn = wave % C::WN;
+
+    uint32_t tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, 8u, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+
+    const int8_t *Ab = A + m0 * Kb;
+    const int8_t *Bb = B + n0 * Kb;
+    const int64_t a_bytes = (int64_t)(M - m0) * Kb;
+    const int64_t b_bytes = (int64_t)(N - n0) * Kb;
+
+    // Per-copy lane offsets inside the tile (constant over K).
+    uint32_t voff[C::NDMA];
+#pragma unroll
+    for (int i = 0; i < C::NDMA; ++i) {
+        const bool isA = i < C::NDMA_A;
+        const int j = (int)wave + C::NW * (isA ? i : i - C::NDMA_A);
+        const int rows = isA ? C::BM / 16 : C::BN / 16;
+        const int rb = j % rows, kb = j / rows;
+        voff[i] = (uint32_t)((rb * 16 + (int)(lane % 16)) * Kb + kb * 64 + (int)(lane / 16) * 16);
+    }
+    const uint32_t smem_base = lds_addr(smem);
+
+    auto issue = [&](int64_t kt, int slot) {
+        const int64_t k0 = kt * C::BK;
+        const i32x4 ra = make_rsrc(Ab + k0, a_bytes > k0 ? (uint64_t)(a_bytes - k0) : 0);
+        const i32x4 rb = make_rsrc(Bb + k0, b_bytes > k0 ? (uint64_t)(b_bytes - k0) : 0);
+        const uint32_t sbase = smem_base + slot * C::STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < C::NDMA; ++i) {
+            const bool isA = i < C::NDMA_A;
+            const int j = (int)wave + C::NW * (isA ? i : i - C::NDMA_A);
+            const uint32_t dst = sbase + (isA ? j : C::ABLK + j) * 1024;
+            dma16(isA ? ra : rb, voff[i], dst);
+        }
+    };
+
+    i32x4 acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+    const int64_t nk = ((int64_t)Kb + C::BK - 1) / C::BK;
+    const bool k_tail = (Kb % C::BK) != 0;
+
+#pragma unroll
+    for (int s = 0; s < C::ST - 1; ++s)
+        if (s < nk) issue(s, s);
+
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int slot = (int)(kt % C::ST);
+        const int64_t after = nk - 1 - kt;
+        wait_outstanding<C::NDMA, C::ST>((int)(after < C::ST - 2 ? after : C::ST - 2));
+        char *stage = smem + slot * C::STAGE_BYTES;
+        if (k_tail && kt == nk - 1) {
+            zero_k_tail<C>(stage, lane, wave, kt * C::BK, Kb);
+            barrier_lds();
+        }
+        if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1, (int)((kt + C::ST - 1) % C::ST));
+
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+            i32x4 af[C::FM], bf[C::FN];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+                af[i] = *(const i32x4 *)(stage + (kb * (C::BM / 16) + wm * C::FM + i) * 1024 + lane * 16);
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                bf[j] = *(const i32x4 *)(stage + (C::ABLK + kb * (C::BN / 16) + wn * C::FN + j) * 1024 + lane * 16);
+            if constexpr (KIND == KIND_S4) {
+                i32x4 alo[C::FM], ahi[C::FM];
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i) {
+                    alo[i] = (af[i] << 4) & (int)0xF0F0F0F0;
+                    ahi[i] = af[i] & (int)0xF0F0F0F0;
+                }
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) {
+                    const i32x4 blo = (bf[j] << 4) & (int)0xF0F0F0F0;
+                    const i32x4 bhi = bf[j] & (int)0xF0F0F0F0;
+#pragma unroll
+                    for (int i = 0; i < C::FM; ++i) {
+                        acc[i][j] = mfma16(blo, alo[i], acc[i][j]);
+                        acc[i][j] = mfma16(bhi, ahi[i], acc[i][j]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma16(bf[j], af[i], acc[i][j]);
+            }
+        }
+    }
+
+    // Epilogue: lane holds C[m][n..n+3] for each fragment.
+    const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int64_t m = m0 + wm * C::TM + i * 16 + (lane % 16);
+        if (m >= M) continue;
+        float scale_m = 0.f;
+        if constexpr (KIND == KIND_LINEAR) scale_m = sx[m];
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const int64_t n = n0 + wn * C::TN + j * 16 + (lane / 16) * 4;
+            if (n >= N) continue;
+            i32x4 v = acc[i][j];
+            if constexpr (KIND == KIND_S4) v = v >> 8;
+            if constexpr (KIND == KIND_LINEAR) {
+                float *o = (float *)out + m * (int64_t)N + n;
+                if (vec_ok) {
+                    const f32x4 s = *(const f32x4 *)(sw + n);
+                    f32x4 r;
+                    r.x = ((float)v.x * scale_m) * s.x;
+                    r.y = ((float)v.y * scale_m) * s.y;
+                    r.z = ((float)v.z * scale_m) * s.z;
+                    r.w = ((float)v.w * scale_m) * s.w;
+                    *(f32x4 *)o = r;
+                } else {
+                    for (int r = 0; r < 4 && n + r < N; ++r) o[r] = ((float)v[r] * scale_m) * sw[n + r];
+                }
+            } else {
+                int32_t *o = (int32_t *)out + m * (int64_t)N + n;
+                if (vec_ok) *(i32x4 *)o = v;
+                else
+                    for (int r = 0; r < 4 && n + r < N; ++r) o[r] = v[r];
+            }
+        }
+    }
+}
+
+// ---- variant table --------------------------------------------------------
+// index = 3*tile + (stages - 2); tile 0 = small, 1 = medium, 2 = large.
+using S2 = MfmaCfg<64, 64, 128, 2, 2, 2>;
+using S3 = MfmaCfg<64, 64, 128, 2, 2, 3>;
+using S4 = MfmaCfg<64, 64, 128, 2, 2, 4>;
+using M2 = MfmaCfg<128, 128, 128, 2, 2, 2>;
+using M3 = MfmaCfg<128, 128, 128, 2, 2, 3>;
+using M4 = MfmaCfg<128, 128, 128, 2, 2, 4>;
+using L2 = MfmaCfg<256, 256, 64, 2, 4, 2>;
+using L3 = MfmaCfg<256, 256, 64, 2, 4, 3>;
+using L4 = MfmaCfg<256, 256, 64, 2, 4, 4>;
+
+template <class C, int KIND>
+static hipError_t launch_one(const void *A, const void *B, void *out, const float *sx,
+                             const float *sw, int64_t M, int64_t N, int64_t Kb, hipStream_t s)
+{
+    const uint64_t tm = (uint64_t)((M + C::BM - 1) / C::BM);
+    const uint64_t tn = (uint64_t)((N + C::BN - 1) / C::BN);
+    if (tm * tn > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mfma_gemm_kernel<C, KIND>), dim3((uint32_t)(tm * tn)), dim3(C::NT), 0, s,
+                       (const int8_t *)A, (const int8_t *)B, out, sx, sw, (int32_t)M, (int32_t)N,
+                       (int32_t)Kb, (uint32_t)tm, (uint32_t)tn);
+    return hipGetLastError();
+}
+
+template <class C>
+static void info_one(int *bm, int *bn, int *bk, int *st)
+{
+    *bm = C::BM; *bn = C::BN; *bk = C::BK; *st = C::ST;
+}
+
+template <int KIND>
+static hipError_t dispatch(int variant, const void *A, const void *B, void *out, const float *sx,
+                           const float *sw, int64_t M, int64_t N, int64_t Kb, hipStream_t s)
+{
+    switch (variant) {
+    case 0: return launch_one<S2, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    case 1: return launch_one<S3, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    case 2: return launch_one<S4, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    case 3: return launch_one<M2, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    case 4: return launch_one<M3, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    case 5: return launch_one<M4, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    case 6: return launch_one<L2, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    case 7: return launch_one<L3, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    case 8: return launch_one<L4, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void *out,
+                       const float *sx, const float *sw, int64_t M, int64_t N, int64_t Kb,
+                       hipStream_t s)
+{
+    switch (kind) {
+    case KIND_S8: return dispatch<KIND_S8>(variant, A, B, out, sx, sw, M, N, Kb, s);
+    case KIND_S4: return dispatch<KIND_S4>(variant, A, B, out, sx, sw, M, N, Kb, s);
+    case KIND_LINEAR: return dispatch<KIND_LINEAR>(variant, A, B, out, sx, sw, M, N, Kb, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+int mfma_variant_info(int variant, int *bm, int *bn, int *bk_bytes, int *stages)
+{
+    switch (variant) {
+    case 0: info_one<S2>(bm, bn, bk_bytes, stages); return 0;
+    case 1: info_one<S3>(bm, bn, bk_bytes, stages); return 0;
+    case 2: info_one<S4>(bm, bn, bk_bytes, stages); return 0;
+    case 3: info_one<M2>(bm, bn, bk_bytes, stages); return 0;
+    case 4: info_one<M3>(bm, bn, bk_bytes, stages); return 0;
+    case 5: info_one<M4>(bm, bn, bk_bytes, stages); return 0;
+    case 6: info_one<L2>(bm, bn, bk_bytes, stages); return 0;
+    case 7: info_one<L3>(bm, bn, bk_bytes, stages); return 0;
+    case 8: info_one<L4>(bm, bn, bk_bytes, stages); return 0;
+    default: return -1;
+    }
+}
+
+}  // namespace lb

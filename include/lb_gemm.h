@@ -1,0 +1,144 @@
+/*
+ * lb_gemm.h -- exact low-bit integer GEMM for AMD MI355X (gfx950).
+ *
+ * The operation is the one stated in the digest of "Leveraging Large-Scale Data
+ * for Efficient Low-Bit CUTLASS GEMM Optimization via Neural Networks" (IEEE
+ * Transactions on Big Data): the matrix product A x B = C for 1-, 4- and 8-bit
+ * operands, computed by a thread-block-tiled kernel whose tile shape and
+ * pipeline depth are chosen per problem (Research results, items 1 and 2), and
+ * used inside a low-bit linear layer (Research results, item 4).  Here every
+ * product is accumulated exactly in int32.
+ *
+ * Plain C: loadable with dlopen/ctypes without HIP headers.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Layout (a reading; the pages fix only A x B = C):
+ *   A    M x K, row-major: row m holds a(m, 0..K-1) contiguously.
+ *   B    K x N, column-major: column n holds b(0..K-1, n) contiguously; these
+ *        are the same bytes as an N x K row-major matrix (an nn.Linear weight).
+ *   C    M x N, row-major, int32.  No leading-dimension arguments: every
+ *        operand is dense.
+ * Packing along K:
+ *   int8  one signed byte per element, values -128..127.
+ *   int4  two signed nibbles per byte (-8..7), even k in the low nibble.
+ *   1-bit 32 elements per uint32, element k in bit (k % 32) of word k / 32;
+ *         the product of two bits is their AND.
+ * Pointers: device pointers (HBM) owned by the caller, readable/writable by the
+ *   current HIP device.  Rows of A and B must start 16-byte aligned, which the
+ *   alignment rule on K below guarantees for a 16-byte-aligned base (hipMalloc
+ *   and torch give 256-byte-aligned bases).  The library does not allocate,
+ *   free, copy or synchronise.
+ * stream: a hipStream_t passed as void*; NULL is the null stream.  Calls are
+ *   asynchronous: a status of LB_OK means the kernel was launched; a fault in
+ *   the kernel surfaces at the caller's next synchronisation.
+ * variant: 0..8 picks a kernel variant, index = 3*tile + (stages - 2) with tile
+ *   0 = small, 1 = medium, 2 = large and stages 2, 3 or 4 (the nine templates:
+ *   three tile sizes times three pipeline depths, Research results, item 2);
+ *   LB_AUTO lets lb_select_variant choose for (dtype, M, N, K).
+ * Errors: every call returns an lb_status and never aborts.  Checks run in this
+ *   order, before any HIP call: null pointer, non-positive size, K alignment,
+ *   variant range, int32 overflow bound; then the launch itself (LB_ERR_HIP).
+ * Thread safety: calls may come from any thread; the only shared state is the
+ *   read-only selection table.
+ */
+#ifndef LB_GEMM_H
+#define LB_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LB_OK = 0,
+    LB_ERR_NULL = 1,     /* a required pointer is NULL */
+    LB_ERR_SHAPE = 2,    /* M, N or K is not positive */
+    LB_ERR_ALIGN = 3,    /* K violates the per-type alignment rule */
+    LB_ERR_VARIANT = 4,  /* variant outside LB_AUTO..8, or dtype unknown */
+    LB_ERR_OVERFLOW = 5, /* K is so large that an int32 sum could overflow */
+    LB_ERR_HIP = 6       /* the HIP runtime reported an error */
+} lb_status;
+
+typedef enum { LB_S8 = 0, LB_S4 = 1, LB_B1 = 2 } lb_dtype;
+
+#define LB_AUTO (-1)
+#define LB_NUM_VARIANTS 9
+#define LB_DEFAULT_VARIANT 7 /* large tile, 3 stages */
+
+/* K limits: rows must be whole 16-byte chunks, and the worst-case |sum| must
+ * fit int32 (16384 * K for int8; the int4 path accumulates 256 * a * b, the
+ * same bound).  1-bit sums are at most K. */
+#define LB_S8_K_ALIGN 16
+#define LB_S4_K_ALIGN 32
+#define LB_B1_K_ALIGN 128
+#define LB_S8_K_MAX 131071
+#define LB_S4_K_MAX 131071
+#define LB_B1_K_MAX 2147483520 /* largest multiple of 128 below 2^31 */
+
+/*
+ * C = A x B, int8 operands, int32 result.
+ *   A: M*K int8 (row-major), B: N*K int8 (column-major K x N), C: M*N int32.
+ *   K: elements (= bytes) per row; K % 16 == 0 and K <= LB_S8_K_MAX.
+ */
+int lb_gemm_s8(const int8_t *A, const int8_t *B, int32_t *C,
+               int64_t M, int64_t N, int64_t K, int variant, void *stream);
+
+/*
+ * C = A x B, signed int4 operands packed two per byte, int32 result.
+ *   A: M*K/2 bytes, B: N*K/2 bytes, C: M*N int32.
+ *   K: int4 elements per row; K % 32 == 0 and K <= LB_S4_K_MAX.
+ */
+int lb_gemm_s4(const uint8_t *A, const uint8_t *B, int32_t *C,
+               int64_t M, int64_t N, int64_t K, int variant, void *stream);
+
+/*
+ * C[m,n] = number of k with bit k set in both row m of A and column n of B.
+ *   A: M*K/32 uint32, B: N*K/32 uint32, C: M*N int32.
+ *   K: bits per row; K % 128 == 0 and K <= LB_B1_K_MAX.
+ */
+int lb_gemm_b1(const uint32_t *A, const uint32_t *B, int32_t *C,
+               int64_t M, int64_t N, int64_t K, int variant, void *stream);
+
+/*
+ * Low-bit linear layer (Research results, item 4): int8 GEMM with the int32
+ * accumulator dequantised in the epilogue, never written to memory:
+ *   out[m*N+n] = ((float)acc[m,n] * sx[m]) * sw[n], fp32, round-to-nearest.
+ *   X: M*K int8 activations (row-major), W: N*K int8 weights (column-major
+ *   K x N, i.e. nn.Linear's [N, K]), sx: M fp32 per-row scales, sw: N fp32
+ *   per-column scales, out: M*N fp32 (row-major).  K as for lb_gemm_s8.
+ */
+int lb_gemm_s8_linear(const int8_t *X, const int8_t *W, const float *sx,
+                      const float *sw, float *out, int64_t M, int64_t N,
+                      int64_t K, int variant, void *stream);
+
+/*
+ * Per-shape variant choice (Research results, items 2-3: the template index is
+ * predicted from M, N, K and the GPU's multiprocessor count, and judged by
+ * whether the true best template is among the top two).
+ *   dtype: an lb_dtype.  M, N, K as for the GEMM of that dtype (K in elements
+ *   or bits).  cu_count: compute units of the target GPU; <= 0 queries the
+ *   current HIP device.  best: receives the chosen variant (0..8).  second:
+ *   receives the runner-up, or may be NULL.
+ * Host-only, microseconds, no GPU work.  Returns LB_ERR_NULL if best is NULL,
+ * LB_ERR_SHAPE for non-positive sizes, LB_ERR_VARIANT for an unknown dtype and
+ * LB_ERR_HIP if cu_count <= 0 and no device can be queried.
+ */
+int lb_select_variant(int dtype, int64_t M, int64_t N, int64_t K, int cu_count,
+                      int *best, int *second);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *lb_status_string(int status);
+
+/* Tile and stage description of a variant for a dtype: writes the workgroup
+ * tile (rows of C, columns of C, K elements per pipeline stage) and the stage
+ * count.  Returns LB_ERR_VARIANT for an index outside 0..8 or unknown dtype. */
+int lb_variant_info(int dtype, int variant, int *tile_m, int *tile_n,
+                    int *tile_k, int *stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LB_GEMM_H */

@@ -1,0 +1,109 @@
+"""CPU tests of the C boundary: the library loads, exports every declared
+symbol, and rejects bad arguments with the documented status codes before any
+HIP call.  No GEMM is launched here (there is no GPU in this container)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_integer_gemm_amd as lb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lb_gemm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lb.LIB_PATH):
+        from bit_integer_gemm_amd import _build
+        _build.build()
+    return lb.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(lb_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(lb.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    def define(name):
+        return int(re.search(rf"#define {name} \(?(-?\d+)\)?", text).group(1))
+    assert define("LB_AUTO") == lb.LB_AUTO
+    assert define("LB_NUM_VARIANTS") == lb.LB_NUM_VARIANTS
+    assert define("LB_DEFAULT_VARIANT") == lb.LB_DEFAULT_VARIANT
+    assert define("LB_S8_K_ALIGN") == lb.K_ALIGN[lb.LB_S8]
+    assert define("LB_S4_K_ALIGN") == lb.K_ALIGN[lb.LB_S4]
+    assert define("LB_B1_K_ALIGN") == lb.K_ALIGN[lb.LB_B1]
+    assert define("LB_S8_K_MAX") == lb.K_MAX[lb.LB_S8]
+    assert define("LB_B1_K_MAX") == lb.K_MAX[lb.LB_B1]
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.mark.parametrize("fn,align,kmax", [("lb_gemm_s8", 16, 131071), ("lb_gemm_s4", 32, 131071),
+                                           ("lb_gemm_b1", 128, 2147483520)])
+def test_gemm_argument_checks(lib, fn, align, kmax):
+    f = getattr(lib, fn)
+    assert f(NULL, FAKE, FAKE, 4, 4, align, -1, NULL) == lb.LB_ERR_NULL
+    assert f(FAKE, NULL, FAKE, 4, 4, align, -1, NULL) == lb.LB_ERR_NULL
+    assert f(FAKE, FAKE, NULL, 4, 4, align, -1, NULL) == lb.LB_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 0, 4, align, -1, NULL) == lb.LB_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, -1, align, -1, NULL) == lb.LB_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 4, 0, -1, NULL) == lb.LB_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 2**31, 4, align, -1, NULL) == lb.LB_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 4, align + align // 2, -1, NULL) == lb.LB_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, 4, 4, align, 9, NULL) == lb.LB_ERR_VARIANT
+    assert f(FAKE, FAKE, FAKE, 4, 4, align, -2, NULL) == lb.LB_ERR_VARIANT
+    over = (kmax // align + 1) * align
+    assert f(FAKE, FAKE, FAKE, 4, 4, over, 0, NULL) == lb.LB_ERR_OVERFLOW
+
+
+def test_linear_argument_checks(lib):
+    f = lib.lb_gemm_s8_linear
+    assert f(FAKE, FAKE, NULL, FAKE, FAKE, 4, 4, 16, -1, NULL) == lb.LB_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, NULL, FAKE, 4, 4, 16, -1, NULL) == lb.LB_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, 4, 4, 16, -1, NULL) == lb.LB_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 24, -1, NULL) == lb.LB_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 131072, -1, NULL) == lb.LB_ERR_OVERFLOW
+
+
+def test_overflow_bound_is_the_int32_limit():
+    # 16384 * K_MAX fits int32, one more K step does not
+    assert 16384 * lb.K_MAX[lb.LB_S8] <= 2**31 - 1 < 16384 * (lb.K_MAX[lb.LB_S8] + 1)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lb.status_string(s) and lb.status_string(s) != "unknown status"
+    assert lb.status_string(99) == "unknown status"
+
+
+def test_variant_info(lib):
+    seen = set()
+    for d in (lb.LB_S8, lb.LB_S4, lb.LB_B1):
+        for v in range(9):
+            info = lb.lb_variant_info(d, v)
+            assert info["stages"] == 2 + v % 3
+            assert info["tile_m"] > 0 and info["tile_n"] > 0 and info["tile_k"] > 0
+            seen.add((d, info["tile_m"] * info["tile_n"]))
+        sizes = [lb.lb_variant_info(d, 3 * t)["tile_m"] * lb.lb_variant_info(d, 3 * t)["tile_n"]
+                 for t in range(3)]
+        assert sizes[0] < sizes[1] < sizes[2]   # small < medium < large
+    # int4 tiles cover twice the K elements of int8 tiles (same bytes)
+    assert lb.lb_variant_info(lb.LB_S4, 7)["tile_k"] == 2 * lb.lb_variant_info(lb.LB_S8, 7)["tile_k"]
+    with pytest.raises(lb.LbError):
+        lb.lb_variant_info(lb.LB_S8, 9)
+    with pytest.raises(lb.LbError):
+        lb.lb_variant_info(3, 0)

@@ -1,0 +1,228 @@
+"""GPU parity: every kernel variant against the CPU oracle, element by element.
+
+All results are integers (the int32 accumulators) and must match bit-exactly;
+the linear layer's fp32 output must be within 1e-6 relative of the oracle's
+fp64 value.  Derivation of that bound: the kernel rounds three times in fp32
+(int32 -> float, times sx, times sw), each with relative error at most 2^-24,
+so the total stays below 3 * 2^-24 + O(2^-48) ~= 1.8e-7 < 1e-6.
+
+Outputs are written into buffers with guard bands on both sides that must come
+back untouched.  Small shapes cover ragged M, N (not multiples of any tile), K
+shorter than one pipeline stage, K not a multiple of the stage, and single rows
+and columns.  The full-size workloads run in the launch configuration the
+benchmark times (automatic variant choice) and are checked on sampled full rows
+and columns against the oracle plus a Freivalds product check over all of C.
+"""
+import numpy as np
+import pytest
+
+import inputs
+import oracle
+
+torch = pytest.importorskip("torch")
+import bit_integer_gemm_amd as lb  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+SENTINEL = 0x5A5A5A5A
+
+
+def to_dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def guarded(M, N, dtype=torch.int32):
+    flat = torch.full((M * N + 2 * GUARD,), SENTINEL if dtype == torch.int32 else float("nan"),
+                      dtype=dtype, device="cuda")
+    return flat, flat[GUARD:GUARD + M * N].view(M, N)
+
+
+def check_guards(flat):
+    head, tail = flat[:GUARD].cpu(), flat[-GUARD:].cpu()
+    if flat.dtype == torch.int32:
+        assert (head == SENTINEL).all() and (tail == SENTINEL).all(), "write outside C"
+    else:
+        assert torch.isnan(head).all() and torch.isnan(tail).all(), "write outside out"
+
+
+def run(kind, A, B, variant, K=None):
+    M, N = A.shape[0], B.shape[0]
+    flat, C = guarded(M, N)
+    dA, dB = to_dev(A), to_dev(B)
+    if kind == "s8":
+        lb.lb_gemm_s8(dA, dB, C, variant)
+    elif kind == "s4":
+        lb.lb_gemm_s4(dA, dB, C, variant)
+    else:
+        lb.lb_gemm_b1(dA.view(torch.int32), dB.view(torch.int32), C, variant)
+    torch.cuda.synchronize()
+    check_guards(flat)
+    return C.cpu().numpy()
+
+
+def make(kind, M, N, K, seed):
+    if kind == "s8":
+        return inputs.s8_rows(M, K, seed), inputs.s8_rows(N, K, seed + 1)
+    if kind == "s4":
+        return inputs.s4_rows(M, K, seed), inputs.s4_rows(N, K, seed + 1)
+    return inputs.b1_rows(M, K, seed), inputs.b1_rows(N, K, seed + 1)
+
+
+def ref(kind, A, B, K):
+    if kind == "s8":
+        return oracle.gemm_s8(A, B)
+    if kind == "s4":
+        return oracle.gemm_s4(A, B, K)
+    return oracle.gemm_b1(A, B, K)
+
+
+SMALL = {
+    "s8": [(256, 256, 256), (1, 1, 16), (63, 65, 48), (257, 129, 272), (130, 300, 112),
+           (64, 64, 2048), (17, 513, 1040), (300, 70, 64)],
+    "s4": [(1, 1, 32), (63, 65, 96), (257, 129, 544), (130, 300, 224), (64, 64, 4096),
+           (17, 513, 2080)],
+    "b1": [(1, 1, 128), (63, 65, 384), (257, 129, 1152), (130, 300, 256), (64, 64, 8192),
+           (17, 513, 2176)],
+}
+
+
+@pytest.mark.parametrize("kind", ["s8", "s4", "b1"])
+@pytest.mark.parametrize("variant", list(range(9)))
+def test_small_shapes_every_variant(kind, variant):
+    for i, (M, N, K) in enumerate(SMALL[kind]):
+        print(f"[parity] {kind} v{variant} M={M} N={N} K={K}", flush=True)
+        A, B = make(kind, M, N, K, 100 + 10 * i)
+        got = run(kind, A, B, variant, K)
+        np.testing.assert_array_equal(got, ref(kind, A, B, K), err_msg=f"{kind} v{variant} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("variant", [lb.LB_AUTO, 0, 4, 7, 8])
+def test_auto_and_variants_mid_size_s8(variant):
+    M, N, K = 520, 776, 1040
+    A, B = make("s8", M, N, K, 900)
+    np.testing.assert_array_equal(run("s8", A, B, variant), oracle.gemm_s8(A, B))
+
+
+def test_extreme_values_at_max_k():
+    """Largest-magnitude operands at the largest K the boundary accepts."""
+    M, N = 33, 47
+    K = 131056  # largest multiple of 16 <= 131071
+    A = np.full((M, K), -128, np.int8)
+    B = np.full((N, K), -128, np.int8)
+    for v in (7, 2, 5):
+        print(f"[parity] s8 extreme v{v}", flush=True)
+        got = run("s8", A, B, v)
+        assert (got == 16384 * K).all()
+    K4 = 131040  # largest multiple of 32 <= 131071
+    A4 = inputs.pack_s4(np.full((M, K4), -8, np.int8))
+    B4 = inputs.pack_s4(np.full((N, K4), 7, np.int8))
+    for v in (7, 2):
+        got = run("s4", A4, B4, v)
+        assert (got == -56 * K4).all()
+    Kb = 8192
+    ones = np.full((M, Kb // 32), 0xFFFFFFFF, np.uint32)
+    for v in (7, 0):
+        assert (run("b1", ones, ones[:1].repeat(N, 0), v) == Kb).all()
+        fives = np.full((M, Kb // 32), 0x55555555, np.uint32)
+        aas = np.full((N, Kb // 32), 0xAAAAAAAA, np.uint32)
+        assert (run("b1", fives, aas, v) == 0).all()
+
+
+def test_transpose_identity_on_gpu():
+    M, N, K = 200, 333, 528
+    A, B = make("s8", M, N, K, 77)
+    np.testing.assert_array_equal(run("s8", B, A, 4), run("s8", A, B, 7).T)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, automatic variant (the benchmark's launch configuration)
+# ---------------------------------------------------------------------------
+
+def sampled_check(kind, A, B, K, C, rng, nrows=6, ncols=6):
+    M, N = C.shape
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, nrows, replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, ncols, replace=False)]))
+    np.testing.assert_array_equal(C[rows], ref(kind, np.ascontiguousarray(A[rows]), B, K))
+    np.testing.assert_array_equal(C[:, cols], ref(kind, A, np.ascontiguousarray(B[cols]), K))
+
+
+def decode(kind, X):
+    if kind == "s8":
+        return X.astype(np.int64)
+    if kind == "s4":
+        p = X.astype(np.uint8)
+        out = np.empty((p.shape[0], p.shape[1] * 2), np.int64)
+        out[:, 0::2] = ((p << 4).astype(np.int8) >> 4)
+        out[:, 1::2] = (p.astype(np.int8) >> 4)
+        return out
+    by = np.ascontiguousarray(X.astype("<u4")).view(np.uint8)
+    return np.unpackbits(by, axis=1, bitorder="little").astype(np.int64)
+
+
+def freivalds(kind, A, B, C, rng, reps=2):
+    """C x == A (B^T x) for random integer vectors x (exact in int64)."""
+    Ad, Bd = decode(kind, A), decode(kind, B)
+    for _ in range(reps):
+        x = rng.integers(-1000, 1000, C.shape[1]).astype(np.int64)
+        np.testing.assert_array_equal(C.astype(np.int64) @ x, Ad @ (Bd.T @ x))
+
+
+@pytest.mark.parametrize("kind,M,N,K,seeds", [
+    ("s4", 4096, 4096, 4096, inputs.SEEDS["s4_4096"]),
+    ("b1", 4096, 4096, 8192, inputs.SEEDS["b1_4096"]),
+    ("s8", 4096, 4096, 4096, (4_000_001, 4_500_001)),
+])
+def test_full_size_sampled(kind, M, N, K, seeds):
+    print(f"[parity] full {kind} {M}x{N}x{K}", flush=True)
+    if kind == "s8":
+        A, B = inputs.s8_rows(M, K, seeds[0]), inputs.s8_rows(N, K, seeds[1])
+    elif kind == "s4":
+        A, B = inputs.s4_rows(M, K, seeds[0]), inputs.s4_rows(N, K, seeds[1])
+    else:
+        A, B = inputs.b1_rows(M, K, seeds[0]), inputs.b1_rows(N, K, seeds[1])
+    C = run(kind, A, B, lb.LB_AUTO, K)
+    g = inputs.rng(12345)
+    sampled_check(kind, A, B, K, C, g)
+    freivalds(kind, A, B, C, g)
+
+
+# ---------------------------------------------------------------------------
+# linear layer
+# ---------------------------------------------------------------------------
+
+def run_linear(X, W, sx, sw, variant):
+    M, N = X.shape[0], W.shape[0]
+    flat, out = guarded(M, N, torch.float32)
+    lb.lb_gemm_s8_linear(to_dev(X), to_dev(W), to_dev(sx), to_dev(sw), out, variant)
+    torch.cuda.synchronize()
+    check_guards(flat)
+    return out.cpu().numpy()
+
+
+def assert_rel(got, want, rtol=1e-6):
+    err = np.abs(got.astype(np.float64) - want)
+    bad = err > rtol * np.abs(want)
+    assert not bad.any(), f"{bad.sum()} elements beyond {rtol} relative; worst {err.max()}"
+
+
+@pytest.mark.parametrize("variant", list(range(9)))
+def test_linear_small_every_variant(variant):
+    for i, (M, N, K) in enumerate([(64, 64, 256), (67, 130, 208), (1, 5, 16), (300, 257, 1040)]):
+        X, W = inputs.s8_rows(M, K, 40 + i), inputs.s8_rows(N, K, 50 + i)
+        sx, sw = inputs.scales(M, 60 + i), inputs.scales(N, 70 + i)
+        assert_rel(run_linear(X, W, sx, sw, variant), oracle.linear_s8(X, W, sx, sw))
+
+
+def test_linear_full_size_sampled():
+    M, K, N = 8192, 4096, 11008
+    s = inputs.SEEDS["linear"]
+    print("[parity] linear full 8192x11008x4096", flush=True)
+    X, W = inputs.s8_rows(M, K, s[0]), inputs.s8_rows(N, K, s[1])
+    sx, sw = inputs.scales(M, s[2]), inputs.scales(N, s[3])
+    out = run_linear(X, W, sx, sw, lb.LB_AUTO)
+    g = inputs.rng(999)
+    rows = np.unique(np.concatenate([[0, M - 1], g.choice(M, 4, replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], g.choice(N, 4, replace=False)]))
+    assert_rel(out[rows], oracle.linear_s8(np.ascontiguousarray(X[rows]), W, sx[rows], sw))
+    assert_rel(out[:, cols], oracle.linear_s8(X, np.ascontiguousarray(W[cols]), sx, sw[cols]))
