@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact low-bit GEMM on one MI355X.
+
+One step is one pass of the whole hot path over the benchmarked workload:
+choose the kernel variant for the shape (host lookup), then run the GEMM on
+operands already resident in HBM.  The default workload is the signed-int4
+GEMM at M = N = K = 4096 (A row-major, B column-major, both packed two per
+byte along K, C int32), on seeded uniform inputs over [-8, 7].
+
+Prints ONE JSON line with the throughput in TOPS (2*M*N*K per GEMM), the
+roofline of the GEMM kernel against MI355X's dense int8 MFMA peak, and the CPU
+oracle timed on a bounded sample of the same workload.  Extra fields report the
+int8 GEMM at 4096^3, the 1-bit GEMM at 4096 x 4096 x 8192 bits and the int8
+linear layer, each with its selected and default variants.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X spec-sheet peaks (dense, no sparsity).
+PEAK_INT8_TOPS = 256 * 2.4e9 * 8192 / 1e12          # 5033.2 TOP/s, int8 MFMA
+PEAK_VALU_B1_TOPS = 256 * 64 * 2.4e9 * 32 / 1e12    # 1258.3 TOP/s (AND+popcount, 2 ops per bit-MAC)
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (dtype, M, N, K, seeds)
+    "s4_gemm_4096": ("s4", 4096, 4096, 4096, (2001, 2002)),
+    "s8_gemm_4096": ("s8", 4096, 4096, 4096, (4_000_001, 4_500_001)),
+    "b1_gemm_4096x4096x8192": ("b1", 4096, 4096, 8192, (3001, 3002)),
+    "s8_linear_8192x11008x4096": ("linear", 8192, 11008, 4096, (5001, 5002, 5003, 5004)),
+    "s8_gemm_256": ("s8", 256, 256, 256, (1001, 1002)),
+}
+
+
+def kernel_source_sha() -> str:
+    d = os.path.join(ROOT, "bit_integer_gemm_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".inc")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def make_operands(dtype, M, N, K, seeds, torch):
+    import inputs
+
+    def d(a):
+        return torch.from_numpy(a).cuda()
+    if dtype == "s8":
+        return d(inputs.s8_rows(M, K, seeds[0])), d(inputs.s8_rows(N, K, seeds[1]))
+    if dtype == "s4":
+        return d(inputs.s4_rows(M, K, seeds[0])), d(inputs.s4_rows(N, K, seeds[1]))
+    if dtype == "b1":
+        return (d(inputs.b1_rows(M, K, seeds[0])).view(torch.int32),
+                d(inputs.b1_rows(N, K, seeds[1])).view(torch.int32))
+    X, W = d(inputs.s8_rows(M, K, seeds[0])), d(inputs.s8_rows(N, K, seeds[1]))
+    return X, W, d(inputs.scales(M, seeds[2])), d(inputs.scales(N, seeds[3]))
+
+
+def step_fn(dtype, ops_, out, lb):
+    """One pass of the hot path: select the variant for the shape, launch the GEMM."""
+    code = {"s8": lb.LB_S8, "s4": lb.LB_S4, "b1": lb.LB_B1, "linear": lb.LB_S8}[dtype]
+    if dtype == "linear":
+        X, W, sx, sw = ops_
+        M, K, N = X.shape[0], X.shape[1], W.shape[0]
+    else:
+        A, B = ops_
+        M, N = A.shape[0], B.shape[0]
+        K = {"s8": A.shape[1], "s4": 2 * A.shape[1], "b1": 32 * A.shape[1]}[dtype]
+
+    def run(variant=None):
+        v = variant
+        if v is None:
+            v, _ = lb.lb_select_variant(code, M, N, K, 0)
+        if dtype == "s8":
+            lb.lb_gemm_s8(A, B, out, v)
+        elif dtype == "s4":
+            lb.lb_gemm_s4(A, B, out, v)
+        elif dtype == "b1":
+            lb.lb_gemm_b1(A, B, out, v)
+        else:
+            lb.lb_gemm_s8_linear(X, W, sx, sw, out, v)
+        return v
+    return run, (M, N, K)
+
+
+def time_steps(run, steps, warmup, torch, variant=None):
+    for _ in range(warmup):
+        run(variant)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        run(variant)
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall   # seconds (HIP events), seconds (host clock)
+
+
+def out_buffer(dtype, M, N, torch):
+    return torch.empty(M, N, dtype=torch.float32 if dtype == "linear" else torch.int32, device="cuda")
+
+
+def load_traffic(workload: str, sha: str):
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None, "no counter profile"
+    t = json.load(open(p))
+    if t.get("kernel_src_sha") != sha:
+        return None, "kernel changed since the counters were taken"
+    return t.get("hbm_bytes_per_launch"), t.get("note")
+
+
+def cpu_baseline(dtype, M, N, K, seeds, rows):
+    """The CPU oracle on the first `rows` rows of A against all of B (a bounded sample)."""
+    import inputs
+    import oracle
+    if dtype == "s4":
+        A, B = inputs.s4_rows(rows, K, seeds[0]), inputs.s4_rows(N, K, seeds[1])
+        f = lambda: oracle.gemm_s4(A, B, K)  # noqa: E731
+    elif dtype == "s8":
+        A, B = inputs.s8_rows(rows, K, seeds[0]), inputs.s8_rows(N, K, seeds[1])
+        f = lambda: oracle.gemm_s8(A, B)  # noqa: E731
+    elif dtype == "b1":
+        A, B = inputs.b1_rows(rows, K, seeds[0]), inputs.b1_rows(N, K, seeds[1])
+        f = lambda: oracle.gemm_b1(A, B, K)  # noqa: E731
+    else:
+        raise ValueError(dtype)
+    oracle.lib()
+    t0 = time.perf_counter()
+    f()
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TOPS",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{dtype} GEMM, first {rows} of {M} rows of A x all {N} columns, K={K} "
+                      f"({rows / M:.1%} of the workload), {dt:.2f} s wall"}
+
+
+def measure(workload, steps, warmup, torch, lb):
+    dtype, M, N, K, seeds = WORKLOADS[workload]
+    ops_ = make_operands(dtype, M, N, K, seeds, torch)
+    out = out_buffer(dtype, M, N, torch)
+    run, (M, N, K) = step_fn(dtype, ops_, out, lb)
+    sel = run()
+    t_sel, wall = time_steps(run, steps, warmup, torch)
+    t_def, _ = time_steps(run, steps, warmup, torch, variant=lb.LB_DEFAULT_VARIANT)
+    ops = 2.0 * M * N * K
+    peak = PEAK_VALU_B1_TOPS if dtype == "b1" else PEAK_INT8_TOPS
+    tops = ops * steps / t_sel / 1e12
+    return {"tops": round(tops, 2), "frac_of_peak": round(tops / peak, 4), "peak_tops": round(peak, 1),
+            "us_per_call": round(t_sel / steps * 1e6, 2), "variant": sel,
+            "default_variant_us": round(t_def / steps * 1e6, 2),
+            "speedup_vs_default": round(t_def / t_sel, 4), "wall_s": round(wall, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="s4_gemm_4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of A in the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="time only the workload (for profiler runs): no extras, no CPU leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB device copy (the reference for HBM byte counters) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the GEMM shards across GPUs without communication, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
+    import bit_integer_gemm_amd as lb
+    lb.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+
+    dtype, M, N, K, seeds = WORKLOADS[args.workload]
+    ops_ = make_operands(dtype, M, N, K, seeds, torch)
+    out = out_buffer(dtype, M, N, torch)
+    run, (M, N, K) = step_fn(dtype, ops_, out, lb)
+    variant = run()
+    torch.cuda.synchronize()
+    t, wall = time_steps(run, args.steps, args.warmup, torch)
+    ms_per_step = t / args.steps * 1e3
+    ops = 2.0 * M * N * K
+    value = ops * args.steps / t / 1e12
+    peak = PEAK_VALU_B1_TOPS if dtype == "b1" else PEAK_INT8_TOPS
+    sha = kernel_source_sha()
+    traffic, traffic_note = load_traffic(args.workload, sha)
+
+    result = {
+        "metric": "low-bit GEMM TOPS (int8/int4/1-bit) at 4096^3; % of chip peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"s4": "int4 (int8 MFMA, int32 acc)", "s8": "int8 (int32 acc)",
+                  "b1": "1-bit (AND+popcount, int32 acc)",
+                  "linear": "int8 (int32 acc) + fp32 dequant"}[dtype],
+        "data": "synthetic (seeded uniform operands, resident in HBM)",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "variant": variant,
+                   "variant_tile": lb.lb_variant_info({"s8": 0, "s4": 1, "b1": 2, "linear": 0}[dtype], variant),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "alu" if dtype == "b1" else "mfma", "achieved": round(value, 2),
+                     "peak": round(peak, 1), "unit": "TOP/s", "frac": round(value / peak, 4),
+                     "traffic": traffic},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
+                   "cu": props.multi_processor_count},
+        "kernel_src_sha": sha,
+        "timed_wall_s": round(wall, 4),
+    }
+    if traffic is None:
+        result["roofline"]["traffic_note"] = traffic_note
+
+    if not args.only and not args.no_extras:
+        extras = {}
+        for w in ("s4_gemm_4096", "s8_gemm_4096", "b1_gemm_4096x4096x8192", "s8_linear_8192x11008x4096"):
+            extras[w] = measure(w, max(10, args.steps // 2), 3, torch, lb)
+        result["extras"] = extras
+
+    if not args.only and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(dtype if dtype != "linear" else "s8", M, N, K, seeds,
+                                              min(args.cpu_rows, M))
+        cb = result["cpu_baseline"]["value"]
+        result["gpu_over_cpu"] = round(value / cb, 1) if cb else None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+"""Shape sweep over the nine kernel variants and the selection table it yields.
+
+This is the data-collection step of the tuning method in the digest of
+"Leveraging Large-Scale Data for Efficient Low-Bit CUTLASS GEMM Optimization via
+Neural Networks" (Research results, item 2): every template (3 tile sizes x 3
+pipeline depths) is timed on each (M, N, K) of a grid on the target GPU, and each
+shape is labelled with its fastest template.  Timings are measured on the GPU
+(median of repeated HIP-event timings, hot caches), not simulated.
+
+  python -m bit_integer_gemm_amd.sweep run   --dtype s8 --out sweep_s8.jsonl
+  python -m bit_integer_gemm_amd.sweep table sweep_s8.jsonl [...] --write
+
+`run` appends one JSON line per (shape, variant) and skips those already in the
+output file, so an interrupted sweep resumes.  It also checks that all nine
+variants return identical C on every shape.  `table` turns measurements into
+labels: the fastest variant, except that the default variant keeps the label
+when it is within EPS of the fastest (timing noise on short kernels must not
+make the selected variant slower than the default), and writes
+csrc/selector_table.inc.
+
+Inputs: for each K, one seeded uniform operand pair of the largest M and N is
+drawn (int8 over [-128, 127], int4 over [-8, 7], Bernoulli(0.5) bits) and each
+shape uses its leading rows, which are contiguous for row-major A and for B's
+(N, K) rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+TABLE = os.path.join(PKG, "csrc", "selector_table.inc")
+
+DTYPES = {"s8": 0, "s4": 1, "b1": 2}
+GRID_MN = [2 ** e for e in range(6, 15)]          # 64 .. 16384
+GRID_K = {"s8": [256, 1024, 4096, 8192], "s4": [256, 1024, 4096, 8192], "b1": [1024, 4096, 8192, 32768]}
+EPS = 0.02
+DEFAULT = 7
+
+
+def time_calls(fn, torch, target_ms=15.0, min_reps=5, max_reps=2000, groups=3):
+    """Median per-call seconds of fn() over `groups` event-timed batches."""
+    fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    est = max(e0.elapsed_time(e1) / 1e3, 1e-6)
+    reps = int(min(max_reps, max(min_reps, math.ceil(target_ms / 1e3 / est / groups))))
+    samples = []
+    for _ in range(groups):
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        samples.append(e0.elapsed_time(e1) / 1e3 / reps)
+    return statistics.median(samples), reps
+
+
+def _operands(dtype, K, torch, Mmax, Nmax):
+    sys.path.insert(0, ROOT)
+    import inputs
+    kidx = GRID_K[dtype].index(K) if K in GRID_K[dtype] else K
+    sa, sb = 4_000_000 + 100 * DTYPES[dtype] + kidx, 4_500_000 + 100 * DTYPES[dtype] + kidx
+    if dtype == "s8":
+        A, B = inputs.s8_rows(Mmax, K, sa), inputs.s8_rows(Nmax, K, sb)
+    elif dtype == "s4":
+        A, B = inputs.s4_rows(Mmax, K, sa), inputs.s4_rows(Nmax, K, sb)
+    else:
+        A, B = inputs.b1_rows(Mmax, K, sa), inputs.b1_rows(Nmax, K, sb)
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    if dtype == "b1":
+        dA, dB = dA.view(torch.int32), dB.view(torch.int32)
+    return dA, dB
+
+
+def run_sweep(dtype, out_path, Ms=None, Ns=None, Ks=None, check=True, log=print):
+    import torch
+    import bit_integer_gemm_amd as lb
+    lb.load()
+    Ms, Ns, Ks = Ms or GRID_MN, Ns or GRID_MN, Ks or GRID_K[dtype]
+    done = set()
+    if os.path.exists(out_path):
+        for line in open(out_path):
+            r = json.loads(line)
+            done.add((r["M"], r["N"], r["K"], r["variant"]))
+    call = {"s8": lb.lb_gemm_s8, "s4": lb.lb_gemm_s4, "b1": lb.lb_gemm_b1}[dtype]
+    f = open(out_path, "a")
+    for K in Ks:
+        dA, dB = _operands(dtype, K, torch, max(Ms), max(Ns))
+        for M in Ms:
+            for N in Ns:
+                todo = [v for v in range(9) if (M, N, K, v) not in done]
+                if not todo:
+                    continue
+                A, B = dA[:M], dB[:N]
+                C = torch.empty(M, N, dtype=torch.int32, device="cuda")
+                ref = None
+                if check:
+                    call(A, B, C, DEFAULT)
+                    ref = C.clone()
+                line_t = []
+                for v in todo:
+                    t, reps = time_calls(lambda: call(A, B, C, v), torch)
+                    agree = bool(torch.equal(C, ref)) if check else None
+                    rec = {"dtype": dtype, "M": M, "N": N, "K": K, "variant": v, "sec": t, "reps": reps,
+                           "tops": 2.0 * M * N * K / t / 1e12, "agrees_with_default": agree}
+                    f.write(json.dumps(rec) + "\n")
+                    line_t.append(f"v{v}:{t * 1e6:.1f}")
+                    if check and not agree:
+                        raise RuntimeError(f"variant {v} disagrees with the default at {dtype} {M}x{N}x{K}")
+                f.flush()
+                del C, ref
+                log(f"[sweep] {dtype} M={M} N={N} K={K} " + " ".join(line_t))
+        del dA, dB
+        torch.cuda.empty_cache()
+    f.close()
+
+
+def load_records(paths):
+    recs = {}
+    for p in paths:
+        for line in open(p):
+            r = json.loads(line)
+            recs[(r["dtype"], r["M"], r["N"], r["K"], r["variant"])] = r
+    return recs
+
+
+def labels(recs, eps=EPS, default=DEFAULT):
+    """{(dtype, M, N, K): (best, second, times[9])} with hysteresis toward the default."""
+    shapes = {}
+    for (d, M, N, K, v), r in recs.items():
+        shapes.setdefault((d, M, N, K), [None] * 9)[v] = r["sec"]
+    out = {}
+    for key, ts in shapes.items():
+        if any(t is None for t in ts):
+            continue
+        order = sorted(range(9), key=lambda v: (ts[v], v))
+        best = order[0]
+        if ts[default] <= (1 + eps) * ts[best]:
+            best = default
+        second = next(v for v in order if v != best)
+        out[key] = (best, second, ts)
+    return out
+
+
+def write_table(lab, path=TABLE):
+    lines = ["// Generated by bit_integer_gemm_amd/sweep.py -- do not edit by hand.",
+             "// Labels from variant timings measured on MI355X (median of HIP-event timings).",
+             "// {dtype, log2(M), log2(N), K, best variant, second variant}",
+             "static const SelEntry kTable[] = {"]
+    items = sorted(lab.items())
+    for (d, M, N, K), (b, s, _) in items:
+        lines.append(f"    {{{DTYPES[d]}, {int(math.log2(M))}, {int(math.log2(N))}, {K}, {b}, {s}}},")
+    if not items:
+        lines.append("    {-1, 0, 0, 1, 7, 8},")
+    lines.append("};")
+    lines.append(f"static const int kTableLen = {len(items)};")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--dtype", choices=sorted(DTYPES), default="s8")
+    r.add_argument("--out", required=True)
+    r.add_argument("--M", type=int, nargs="*")
+    r.add_argument("--N", type=int, nargs="*")
+    r.add_argument("--K", type=int, nargs="*")
+    r.add_argument("--no-check", action="store_true")
+    t = sub.add_parser("table")
+    t.add_argument("files", nargs="+")
+    t.add_argument("--write", action="store_true")
+    a = ap.parse_args(argv)
+    if a.cmd == "run":
+        t0 = time.time()
+        run_sweep(a.dtype, a.out, a.M, a.N, a.K, check=not a.no_check,
+                  log=lambda s: print(s, flush=True))
+        print(f"[sweep] done in {time.time() - t0:.1f} s", flush=True)
+    else:
+        lab = labels(load_records(a.files))
+        n_def = sum(1 for (b, _, _) in lab.values() if b == DEFAULT)
+        print(f"{len(lab)} shapes labelled; default kept on {n_def}")
+        if a.write:
+            write_table(lab)
+            print(f"wrote {TABLE}")
+
+
+if __name__ == "__main__":
+    main()
