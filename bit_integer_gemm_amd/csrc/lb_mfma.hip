@@ -11,12 +11,13 @@
 //  * One workgroup per BM x BN tile of C, NW waves in a WM x WN grid; each wave
 //    owns a (BM/WM) x (BN/WN) sub-tile held in int32 accumulators.
 //  * K is walked in stages of BK bytes.  A stage is an LDS buffer holding the
-//    A and B slices as 1 KiB "fragment blocks": 16 rows x 64 K-bytes, stored in
-//    the order the MFMA consumes them (lane i's 16 bytes at offset 16*i, lane i
-//    covering row i%16 and K-bytes 16*(i/16)..+15).  A copy instruction fills
-//    exactly one block, so LDS reads are 1 KiB contiguous per wave (no bank
-//    conflicts) and each lane's global read is a 16-byte piece of a 64-byte
-//    row segment.
+//    A and B slices as 1 KiB blocks of 16 rows x 64 K-bytes.  One copy
+//    instruction fills one block: lanes 4r..4r+3 fetch the four 16-byte
+//    chunks of row r (one contiguous 64-byte segment, so the address
+//    coalescer merges them; spreading consecutive lanes over 16 rows instead
+//    cuts delivered bandwidth by 2-3x), and the chunk order inside each row
+//    is XOR-permuted by (r/4)%4.  The MFMA fragment read (lane i takes row
+//    i%16, chunk i/16) then hits 16 distinct 16-byte bank groups per 16 lanes.
 //  * ST stages (2, 3 or 4) form a ring filled by direct global->LDS copies
 //    issued ST-1 stages ahead (the multi-stage pipeline of Research results
 //    item 1; the 2-stage case is classic double buffering).
@@ -54,6 +55,16 @@ struct MfmaCfg {
     static_assert(ST * STAGE_BYTES <= 160 * 1024, "LDS");
 };
 
+// Layout of a 16-row x 64-byte block: row r's chunk c sits at 16-byte slot
+// 4*r + (c ^ ((r >> 2) & 3)).
+__device__ inline uint32_t blk_row_of_lane(uint32_t lane) { return lane >> 2; }
+__device__ inline uint32_t blk_chunk_of_lane(uint32_t lane) { return (lane & 3u) ^ ((lane >> 4) & 3u); }
+__device__ inline uint32_t frag_offset(uint32_t lane)
+{
+    const uint32_t r = lane & 15u, c = lane >> 4;
+    return (4u * r + (c ^ ((r >> 2) & 3u))) * 16u;
+}
+
 // Out-of-range K pieces of A in the last (partial) stage are zeroed in LDS:
 // with A's extra K at zero, whatever B holds there contributes nothing.
 template <class C>
@@ -64,7 +75,7 @@ __device__ inline void zero_k_tail(char *stage, uint32_t lane, uint32_t wave,
     for (int i = 0; i < C::NDMA_A; ++i) {
         const int j = (int)wave + C::NW * i;
         const int kb = j / (C::BM / 16);
-        const int64_t kbyte = k0 + kb * 64 + (int)(lane / 16) * 16;
+        const int64_t kbyte = k0 + kb * 64 + (int)blk_chunk_of_lane(lane) * 16;
         if (kbyte >= Kb)
             *(i32x4 *)(stage + j * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
     }
@@ -119,7 +130,8 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
         const int j = (int)wave + C::NW * (isA ? i : i - C::NDMA_A);
         const int rows = isA ? C::BM / 16 : C::BN / 16;
         const int rb = j % rows, kb = j / rows;
-        voff[i] = (uint32_t)((rb * 16 + (int)(lane % 16)) * Kb + kb * 64 + (int)(lane / 16) * 16);
+        voff[i] = (uint32_t)((rb * 16 + (int)blk_row_of_lane(lane)) * Kb + kb * 64 +
+                             (int)blk_chunk_of_lane(lane) * 16);
     }
     const uint32_t smem_base = lds_addr(smem);
 
@@ -161,15 +173,16 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
         }
         if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1, (int)((kt + C::ST - 1) % C::ST));
 
+        const char *fstage = stage + frag_offset(lane);
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
             i32x4 af[C::FM], bf[C::FN];
 #pragma unroll
             for (int i = 0; i < C::FM; ++i)
-                af[i] = *(const i32x4 *)(stage + (kb * (C::BM / 16) + wm * C::FM + i) * 1024 + lane * 16);
+                af[i] = *(const i32x4 *)(fstage + (kb * (C::BM / 16) + wm * C::FM + i) * 1024);
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
-                bf[j] = *(const i32x4 *)(stage + (C::ABLK + kb * (C::BN / 16) + wn * C::FN + j) * 1024 + lane * 16);
+                bf[j] = *(const i32x4 *)(fstage + (C::ABLK + kb * (C::BN / 16) + wn * C::FN + j) * 1024);
             if constexpr (KIND == KIND_S4) {
                 i32x4 alo[C::FM], ahi[C::FM];
 #pragma unroll
@@ -235,15 +248,22 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
 
 // ---- variant table --------------------------------------------------------
 // index = 3*tile + (stages - 2); tile 0 = small, 1 = medium, 2 = large.
-using S2 = MfmaCfg<64, 64, 128, 2, 2, 2>;
-using S3 = MfmaCfg<64, 64, 128, 2, 2, 3>;
-using S4 = MfmaCfg<64, 64, 128, 2, 2, 4>;
-using M2 = MfmaCfg<128, 128, 128, 2, 2, 2>;
-using M3 = MfmaCfg<128, 128, 128, 2, 2, 3>;
-using M4 = MfmaCfg<128, 128, 128, 2, 2, 4>;
-using L2 = MfmaCfg<256, 256, 64, 2, 4, 2>;
-using L3 = MfmaCfg<256, 256, 64, 2, 4, 3>;
-using L4 = MfmaCfg<256, 256, 64, 2, 4, 4>;
+// Each tile has an LDS budget; the K depth of a stage (BK bytes) is chosen so
+// that the stage count fits it: more stages hide more latency but take more
+// LDS per workgroup and so allow fewer workgroups per CU, the trade-off of
+// Research results item 1.  Measured on MI355X at 4096^3 int8: a medium tile
+// with two 32 KiB stages (two workgroups per CU) runs in 66 us while the same
+// tile with three 32 KiB stages (one workgroup per CU) needs 105 us, hence
+// 64-byte stages for the deeper medium and large pipelines.
+using S2 = MfmaCfg<64, 64, 128, 2, 2, 2>;     // 32 KiB
+using S3 = MfmaCfg<64, 64, 128, 2, 2, 3>;     // 48 KiB
+using S4 = MfmaCfg<64, 64, 128, 2, 2, 4>;     // 64 KiB
+using M2 = MfmaCfg<128, 128, 128, 2, 2, 2>;   // 64 KiB
+using M3 = MfmaCfg<128, 128, 64, 2, 2, 3>;    // 48 KiB
+using M4 = MfmaCfg<128, 128, 64, 2, 2, 4>;    // 64 KiB
+using L2 = MfmaCfg<256, 256, 128, 4, 4, 2>;   // 128 KiB, 16 waves of 64x64
+using L3 = MfmaCfg<256, 256, 64, 4, 4, 3>;    // 96 KiB
+using L4 = MfmaCfg<256, 256, 64, 4, 4, 4>;    // 128 KiB
 
 template <class C, int KIND>
 static hipError_t launch_one(const void *A, const void *B, void *out, const float *sx,

@@ -44,7 +44,7 @@ EPS = 0.02
 DEFAULT = 7
 
 
-def time_calls(fn, torch, target_ms=15.0, min_reps=5, max_reps=2000, groups=3):
+def time_calls(fn, torch, target_ms=12.0, min_reps=3, max_reps=2000, groups=3):
     """Median per-call seconds of fn() over `groups` event-timed batches."""
     fn()
     torch.cuda.synchronize()
@@ -110,11 +110,13 @@ def run_sweep(dtype, out_path, Ms=None, Ns=None, Ks=None, check=True, log=print)
                     call(A, B, C, DEFAULT)
                     ref = C.clone()
                 line_t = []
+                sel = lb.lb_select_variant(DTYPES[dtype], M, N, K, 0)
                 for v in todo:
                     t, reps = time_calls(lambda: call(A, B, C, v), torch)
                     agree = bool(torch.equal(C, ref)) if check else None
                     rec = {"dtype": dtype, "M": M, "N": N, "K": K, "variant": v, "sec": t, "reps": reps,
-                           "tops": 2.0 * M * N * K / t / 1e12, "agrees_with_default": agree}
+                           "tops": 2.0 * M * N * K / t / 1e12, "agrees_with_default": agree,
+                           "selected": sel[0], "second": sel[1]}
                     f.write(json.dumps(rec) + "\n")
                     line_t.append(f"v{v}:{t * 1e6:.1f}")
                     if check and not agree:
@@ -170,6 +172,52 @@ def write_table(lab, path=TABLE):
         f.write("\n".join(lines) + "\n")
 
 
+def evaluate(table_files, eval_files, eps=EPS, default=DEFAULT):
+    """Score the compiled selection against an independent timing run.
+
+    Uses the `selected`/`second` fields recorded by `run` (what the library's
+    lb_select_variant returned) and the second run's timings as truth.
+    """
+    recs = load_records(eval_files)
+    shapes = {}
+    sel = {}
+    for (d, M, N, K, v), r in recs.items():
+        shapes.setdefault((d, M, N, K), [None] * 9)[v] = r["sec"]
+        sel[(d, M, N, K)] = (r.get("selected"), r.get("second"))
+    rows = []
+    for key, ts in sorted(shapes.items()):
+        if any(t is None for t in ts):
+            continue
+        b, s2 = sel[key]
+        best = min(range(9), key=lambda v: (ts[v], v))
+        rows.append({"shape": key, "t": ts, "sel": b, "second": s2, "best": best})
+    n = len(rows)
+    if not n:
+        return {"shapes": 0}
+    viol = [r for r in rows if r["t"][r["sel"]] > (1 + eps) * r["t"][default]]
+    sp_def = [r["t"][default] / r["t"][r["sel"]] for r in rows]
+    sp_best = [r["t"][r["best"]] / r["t"][r["sel"]] for r in rows]
+    # best single fixed variant: lowest geometric-mean slowdown vs per-shape best
+    def gm(xs):
+        return math.exp(sum(math.log(x) for x in xs) / len(xs))
+    fixed = min(range(9), key=lambda v: gm([r["t"][v] / r["t"][r["best"]] for r in rows]))
+    sp_fixed = [r["t"][fixed] / r["t"][r["sel"]] for r in rows]
+    near = lambda r, v: r["t"][v] <= (1 + eps) * r["t"][r["best"]]  # noqa: E731
+    top1 = sum(1 for r in rows if r["sel"] == r["best"]) / n
+    top2 = sum(1 for r in rows if r["best"] in (r["sel"], r["second"])) / n
+    top1e = sum(1 for r in rows if near(r, r["sel"])) / n
+    return {
+        "shapes": n, "eps": eps, "default_variant": default,
+        "violations_slower_than_default": len(viol),
+        "violation_shapes": [r["shape"] for r in viol],
+        "speedup_vs_default": {"geomean": gm(sp_def), "max": max(sp_def), "min": min(sp_def)},
+        "best_fixed_variant": fixed,
+        "speedup_vs_best_fixed": {"geomean": gm(sp_fixed), "max": max(sp_fixed), "min": min(sp_fixed)},
+        "selected_vs_oracle_best": {"geomean": gm(sp_best), "min": min(sp_best)},
+        "top1_accuracy": top1, "top2_accuracy": top2, "top1_within_eps": top1e,
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -183,12 +231,22 @@ def main(argv=None):
     t = sub.add_parser("table")
     t.add_argument("files", nargs="+")
     t.add_argument("--write", action="store_true")
+    e = sub.add_parser("evaluate")
+    e.add_argument("files", nargs="+", help="timing runs made with the compiled table")
+    e.add_argument("--json", help="write the report here")
     a = ap.parse_args(argv)
     if a.cmd == "run":
         t0 = time.time()
         run_sweep(a.dtype, a.out, a.M, a.N, a.K, check=not a.no_check,
                   log=lambda s: print(s, flush=True))
         print(f"[sweep] done in {time.time() - t0:.1f} s", flush=True)
+    elif a.cmd == "evaluate":
+        rep = evaluate(None, a.files)
+        txt = json.dumps(rep, indent=1)
+        print(txt)
+        if a.json:
+            with open(a.json, "w") as f:
+                f.write(txt + "\n")
     else:
         lab = labels(load_records(a.files))
         n_def = sum(1 for (b, _, _) in lab.values() if b == DEFAULT)
