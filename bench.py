@@ -1,17 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the exact low-bit GEMM on one MI355X.
 
-One step is one pass of the whole hot path over the benchmarked workload:
-choose the kernel variant for the shape (host lookup), then run the GEMM on
-operands already resident in HBM.  The default workload is the signed-int4
+One step is one pass of the whole hot path over the benchmarked workload: one
+library call with automatic variant choice (the library looks the shape up in
+its selection table, then launches the chosen kernel) on operands already
+resident in HBM.  The default workload is the signed-int4
 GEMM at M = N = K = 4096 (A row-major, B column-major, both packed two per
 byte along K, C int32), on seeded uniform inputs over [-8, 7].
 
 Prints ONE JSON line with the throughput in TOPS (2*M*N*K per GEMM), the
 roofline of the GEMM kernel against MI355X's dense int8 MFMA peak, and the CPU
 oracle timed on a bounded sample of the same workload.  Extra fields report the
-int8 GEMM at 4096^3, the 1-bit GEMM at 4096 x 4096 x 8192 bits and the int8
-linear layer, each with its selected and default variants.
+int4 and int8 GEMMs at 4096^3, the 1-bit GEMM at 4096 x 4096 x 8192 bits and the
+int8 linear layer, each with its selected and default variants (kernel time from
+HIP-graph replays, so that host launch cost is excluded).
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
 """
@@ -80,9 +82,8 @@ def step_fn(dtype, ops_, out, lb):
         K = {"s8": A.shape[1], "s4": 2 * A.shape[1], "b1": 32 * A.shape[1]}[dtype]
 
     def run(variant=None):
-        v = variant
-        if v is None:
-            v, _ = lb.lb_select_variant(code, M, N, K, 0)
+        # variant None = LB_AUTO: the library picks the variant for the shape on every call
+        v = lb.LB_AUTO if variant is None else variant
         if dtype == "s8":
             lb.lb_gemm_s8(A, B, out, v)
         elif dtype == "s4":
@@ -92,6 +93,10 @@ def step_fn(dtype, ops_, out, lb):
         else:
             lb.lb_gemm_s8_linear(X, W, sx, sw, out, v)
         return v
+
+    def selected():
+        return lb.lb_select_variant(code, M, N, K, 0)[0]
+    run.selected = selected
     return run, (M, N, K)
 
 
@@ -150,21 +155,23 @@ def cpu_baseline(dtype, M, N, K, seeds, rows):
                       f"({rows / M:.1%} of the workload), {dt:.2f} s wall"}
 
 
-def measure(workload, steps, warmup, torch, lb):
+def measure(workload, torch, lb):
+    """Selected and default variant of one workload, kernel time only (HIP-graph replay)."""
+    from bit_integer_gemm_amd.sweep import time_calls
     dtype, M, N, K, seeds = WORKLOADS[workload]
     ops_ = make_operands(dtype, M, N, K, seeds, torch)
     out = out_buffer(dtype, M, N, torch)
     run, (M, N, K) = step_fn(dtype, ops_, out, lb)
-    sel = run()
-    t_sel, wall = time_steps(run, steps, warmup, torch)
-    t_def, _ = time_steps(run, steps, warmup, torch, variant=lb.LB_DEFAULT_VARIANT)
+    sel = run.selected()
+    t_sel, _ = time_calls(lambda: run(sel), torch, target_ms=30.0, groups=5)
+    t_def, _ = time_calls(lambda: run(lb.LB_DEFAULT_VARIANT), torch, target_ms=30.0, groups=5)
     ops = 2.0 * M * N * K
     peak = PEAK_VALU_B1_TOPS if dtype == "b1" else PEAK_INT8_TOPS
-    tops = ops * steps / t_sel / 1e12
+    tops = ops / t_sel / 1e12
     return {"tops": round(tops, 2), "frac_of_peak": round(tops / peak, 4), "peak_tops": round(peak, 1),
-            "us_per_call": round(t_sel / steps * 1e6, 2), "variant": sel,
-            "default_variant_us": round(t_def / steps * 1e6, 2),
-            "speedup_vs_default": round(t_def / t_sel, 4), "wall_s": round(wall, 4)}
+            "us_per_call": round(t_sel * 1e6, 2), "variant": sel,
+            "default_variant_us": round(t_def * 1e6, 2),
+            "speedup_vs_default": round(t_def / t_sel, 4)}
 
 
 def main():
@@ -207,7 +214,8 @@ def main():
     ops_ = make_operands(dtype, M, N, K, seeds, torch)
     out = out_buffer(dtype, M, N, torch)
     run, (M, N, K) = step_fn(dtype, ops_, out, lb)
-    variant = run()
+    variant = run.selected()
+    run()
     torch.cuda.synchronize()
     t, wall = time_steps(run, args.steps, args.warmup, torch)
     ms_per_step = t / args.steps * 1e3
@@ -249,7 +257,7 @@ def main():
     if not args.only and not args.no_extras:
         extras = {}
         for w in ("s4_gemm_4096", "s8_gemm_4096", "b1_gemm_4096x4096x8192", "s8_linear_8192x11008x4096"):
-            extras[w] = measure(w, max(10, args.steps // 2), 3, torch, lb)
+            extras[w] = measure(w, torch, lb)
         result["extras"] = extras
 
     if not args.only and not args.no_cpu_baseline:

