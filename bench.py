@@ -15,7 +15,7 @@ int4 and int8 GEMMs at 4096^3, the 1-bit GEMM at 4096 x 4096 x 8192 bits and the
 int8 linear layer, each with its selected and default variants (kernel time from
 HIP-graph replays, so that host launch cost is excluded).
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+Usage: python bench.py [--gpus 1] [--steps 300] [--warmup 100]
 """
 from __future__ import annotations
 
@@ -177,8 +177,10 @@ def measure(workload, torch, lb):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--prewarm-ms", type=float, default=150.0,
+                    help="untimed steps before the warmup steps, to let the GPU reach steady clocks")
     ap.add_argument("--workload", default="s4_gemm_4096", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of A in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -217,6 +219,14 @@ def main():
     variant = run.selected()
     run()
     torch.cuda.synchronize()
+    # The GPU raises its clocks over the first ~30 ms of sustained work; run
+    # untimed steps for at least args.prewarm_ms before the warmup steps so that
+    # the timed steps see steady-state clocks.
+    t_end = time.perf_counter() + args.prewarm_ms / 1e3
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            run()
+        torch.cuda.synchronize()
     t, wall = time_steps(run, args.steps, args.warmup, torch)
     ms_per_step = t / args.steps * 1e3
     ops = 2.0 * M * N * K

@@ -9,11 +9,14 @@
 // the labels come from timings measured on MI355X and compiled in as a table
 // (selector_table.inc, written by the package's sweep tool); a query takes the
 // label of the nearest measured shape in log2 space.  Shapes of a dtype with
-// no measurements get the default variant.
+// no measurements get the default variant.  With LB_SELECTOR=mlp in the
+// environment the pages' feed-forward classifier decides instead.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 
 #include "lb_gemm.h"
 #include "lb_internal.hpp"
@@ -28,6 +31,61 @@ struct SelEntry {
 };
 
 #include "selector_table.inc"
+#include "selector_mlp.inc"
+
+// The pages' classifier (Research results item 3): 4 inputs (log2 M, log2 N,
+// log2 K each divided by 16, CU count divided by 256) -> three ReLU layers of
+// 128 -> 9 logits.  Weights trained offline on measured sweeps, stored as fp32
+// bit patterns.
+float bits_to_float(uint32_t u)
+{
+    float f;
+    std::memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+void dense(const uint32_t *W, const uint32_t *b, const float *in, int fin, float *out, int fout,
+           bool relu)
+{
+    for (int o = 0; o < fout; ++o) {
+        float acc = 0.f;
+        for (int i = 0; i < fin; ++i) acc += bits_to_float(W[o * fin + i]) * in[i];
+        acc += bits_to_float(b[o]);
+        out[o] = relu && acc < 0.f ? 0.f : acc;
+    }
+}
+
+void mlp_logits(int dtype, int64_t M, int64_t N, int64_t K, int cu, float *logits)
+{
+    const uint32_t *W[4], *B[4];
+    switch (dtype) {
+    case 0:
+        W[0] = kMlpW0_0; W[1] = kMlpW0_1; W[2] = kMlpW0_2; W[3] = kMlpW0_3;
+        B[0] = kMlpB0_0; B[1] = kMlpB0_1; B[2] = kMlpB0_2; B[3] = kMlpB0_3;
+        break;
+    case 1:
+        W[0] = kMlpW1_0; W[1] = kMlpW1_1; W[2] = kMlpW1_2; W[3] = kMlpW1_3;
+        B[0] = kMlpB1_0; B[1] = kMlpB1_1; B[2] = kMlpB1_2; B[3] = kMlpB1_3;
+        break;
+    default:
+        W[0] = kMlpW2_0; W[1] = kMlpW2_1; W[2] = kMlpW2_2; W[3] = kMlpW2_3;
+        B[0] = kMlpB2_0; B[1] = kMlpB2_1; B[2] = kMlpB2_2; B[3] = kMlpB2_3;
+        break;
+    }
+    float x[4] = {(float)(std::log2((double)M) / 16.0), (float)(std::log2((double)N) / 16.0),
+                  (float)(std::log2((double)K) / 16.0), (float)(cu / 256.0)};
+    float h1[LB_MLP_HIDDEN], h2[LB_MLP_HIDDEN];
+    dense(W[0], B[0], x, 4, h1, LB_MLP_HIDDEN, true);
+    dense(W[1], B[1], h1, LB_MLP_HIDDEN, h2, LB_MLP_HIDDEN, true);
+    dense(W[2], B[2], h2, LB_MLP_HIDDEN, h1, LB_MLP_HIDDEN, true);
+    dense(W[3], B[3], h1, LB_MLP_HIDDEN, logits, LB_NUM_VARIANTS, false);
+}
+
+bool use_mlp(int dtype)
+{
+    const char *e = std::getenv("LB_SELECTOR");
+    return e && std::strcmp(e, "mlp") == 0 && dtype >= 0 && dtype < 3 && kMlpPresent[dtype];
+}
 
 std::atomic<int> g_cu_cache[64];
 
@@ -57,6 +115,19 @@ int select_from_table(int dtype, int64_t M, int64_t N, int64_t K, int cu_count, 
     if (cu_count <= 0) {
         int st = device_cu_count(&cu_count);
         if (st != LB_OK) return st;
+    }
+    if (use_mlp(dtype)) {
+        float lg[LB_NUM_VARIANTS];
+        mlp_logits(dtype, M, N, K, cu_count, lg);
+        int b0 = 0;
+        for (int v = 1; v < LB_NUM_VARIANTS; ++v)
+            if (lg[v] > lg[b0]) b0 = v;
+        int b1 = b0 == 0 ? 1 : 0;
+        for (int v = 0; v < LB_NUM_VARIANTS; ++v)
+            if (v != b0 && lg[v] > lg[b1]) b1 = v;
+        *best = b0;
+        if (second) *second = b1;
+        return LB_OK;
     }
     const double lm = std::log2((double)M), ln = std::log2((double)N), lk = std::log2((double)K);
     int bi = -1;

@@ -1,0 +1,117 @@
+"""CPU tests of the variant selector (host logic only; no kernel is launched).
+
+Table mode: every measured shape must map to its own label, off-grid shapes to
+the label of the nearest measured shape in log2 space, computed here
+independently from the generated table text.  Classifier mode (LB_SELECTOR=mlp):
+the library's C++ forward pass must pick the same top-2 variants as a numpy
+forward pass over the same exported weights.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_integer_gemm_amd as lb
+from bit_integer_gemm_amd import selector_mlp
+
+TABLE = os.path.join(os.path.dirname(lb.__file__), "csrc", "selector_table.inc")
+
+
+def table_entries():
+    text = open(TABLE).read()
+    n = int(re.search(r"kTableLen = (\d+);", text).group(1))
+    rows = re.findall(r"\{(-?\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\}", text)
+    return [tuple(int(x) for x in r) for r in rows][:n]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    if not os.path.exists(lb.LIB_PATH):
+        from bit_integer_gemm_amd import _build
+        _build.build()
+    lb.load()
+    old = os.environ.pop("LB_SELECTOR", None)
+    yield
+    if old is not None:
+        os.environ["LB_SELECTOR"] = old
+
+
+def test_table_has_all_dtypes_and_valid_labels():
+    ents = table_entries()
+    assert ents, "selection table is empty"
+    assert {e[0] for e in ents} == {0, 1, 2}
+    for d, lm, ln, k, b, s in ents:
+        assert 0 <= b < 9 and 0 <= s < 9 and b != s
+
+
+def test_measured_shapes_map_to_their_labels():
+    for d, lm, ln, k, b, s in table_entries():
+        assert lb.lb_select_variant(d, 2 ** lm, 2 ** ln, k, 256) == (b, s)
+
+
+def test_off_grid_shapes_take_nearest_label():
+    ents = table_entries()
+    g = np.random.Generator(np.random.PCG64(5))
+    for _ in range(300):
+        d = int(g.integers(0, 3))
+        M, N = int(g.integers(1, 40000)), int(g.integers(1, 40000))
+        K = int(g.integers(1, 70000))
+        cand = [e for e in ents if e[0] == d]
+        dist = [abs(math.log2(M) - e[1]) + abs(math.log2(N) - e[2]) + abs(math.log2(K) - math.log2(e[3]))
+                for e in cand]
+        best = min(dist)
+        ok = {(e[4], e[5]) for e, dd in zip(cand, dist) if dd <= best + 1e-9}
+        assert lb.lb_select_variant(d, M, N, K, 256) in ok, (d, M, N, K)
+
+
+def test_selector_argument_errors():
+    f = lb.load().lb_select_variant
+    b, s = ctypes.c_int(), ctypes.c_int()
+    assert f(0, 16, 16, 16, 256, None, None) == lb.LB_ERR_NULL
+    assert f(0, 0, 16, 16, 256, ctypes.byref(b), None) == lb.LB_ERR_SHAPE
+    assert f(3, 16, 16, 16, 256, ctypes.byref(b), None) == lb.LB_ERR_VARIANT
+    assert f(2, 16, 16, 16, 256, ctypes.byref(b), None) == lb.LB_OK   # second may be NULL
+
+
+def test_device_query_fails_cleanly_without_gpu():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    b = ctypes.c_int()
+    assert lb.load().lb_select_variant(0, 64, 64, 64, 0, ctypes.byref(b), None) == lb.LB_ERR_HIP
+
+
+def test_classifier_matches_numpy_forward():
+    weights = selector_mlp.read_inc()
+    assert set(weights) == {0, 1, 2}
+    for code, ws in weights.items():
+        assert [W.shape for W, _ in ws] == [(128, 4), (128, 128), (128, 128), (9, 128)]
+    g = np.random.Generator(np.random.PCG64(9))
+    os.environ["LB_SELECTOR"] = "mlp"
+    try:
+        checked = 0
+        for _ in range(400):
+            d = int(g.integers(0, 3))
+            M, N, K = (int(2 ** g.uniform(5, 15)) for _ in range(3))
+            lg = selector_mlp.forward_np(weights[d], selector_mlp.features(M, N, K, 256))
+            order = np.argsort(-lg)
+            if lg[order[0]] - lg[order[1]] < 1e-4 or lg[order[1]] - lg[order[2]] < 1e-4:
+                continue   # near-tie: fp32 summation order may legitimately flip it
+            assert lb.lb_select_variant(d, M, N, K, 256) == (int(order[0]), int(order[1])), (d, M, N, K)
+            checked += 1
+        assert checked > 300
+    finally:
+        del os.environ["LB_SELECTOR"]
+
+
+def test_classifier_layer_math_by_hand():
+    """One hand-built two-unit layer through forward_np: the reference itself is pinned."""
+    W = np.array([[1.0, -2.0], [0.5, 0.5]], np.float32)
+    b = np.array([0.25, -3.0], np.float32)
+    W2 = np.array([[2.0, 1.0]], np.float32)
+    out = selector_mlp.forward_np([(W, b), (W2, np.zeros(1, np.float32))], [3.0, 1.0])
+    # hidden = relu([3 - 2 + 0.25, 1.5 + 0.5 - 3]) = [1.25, 0]; out = 2 * 1.25
+    assert out.tolist() == [2.5]
