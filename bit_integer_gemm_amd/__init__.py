@@ -28,7 +28,7 @@ LB_AUTO = -1
 LB_NUM_VARIANTS = 9
 LB_DEFAULT_VARIANT = 7
 K_ALIGN = {LB_S8: 16, LB_S4: 32, LB_B1: 128}
-K_MAX = {LB_S8: 131071, LB_S4: 131071, LB_B1: 2147483520}
+K_MAX = {LB_S8: 131071, LB_S4: 131071, LB_B1: 134217600}
 
 # Exported symbols of include/lb_gemm.h (checked by the CPU tests).
 EXPORTS = ("lb_gemm_s8", "lb_gemm_s4", "lb_gemm_b1", "lb_gemm_s8_linear",

@@ -92,7 +92,7 @@ const char *lb_status_string(int status)
     case LB_ERR_SHAPE: return "non-positive or too large M, N or K";
     case LB_ERR_ALIGN: return "K violates the alignment rule for this type";
     case LB_ERR_VARIANT: return "variant or dtype out of range";
-    case LB_ERR_OVERFLOW: return "K too large for an exact int32 sum";
+    case LB_ERR_OVERFLOW: return "K above the limit for this type (exact int32 sum, or 1-bit addressing)";
     case LB_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
     }

@@ -38,7 +38,7 @@
  *   LB_AUTO lets lb_select_variant choose for (dtype, M, N, K).
  * Errors: every call returns an lb_status and never aborts.  Checks run in this
  *   order, before any HIP call: null pointer, non-positive size, K alignment,
- *   variant range, int32 overflow bound; then the launch itself (LB_ERR_HIP).
+ *   variant range, K limit; then the launch itself (LB_ERR_HIP).
  * Thread safety: calls may come from any thread; the only shared state is the
  *   read-only selection table.
  */
@@ -57,7 +57,7 @@ typedef enum {
     LB_ERR_SHAPE = 2,    /* M, N or K is not positive */
     LB_ERR_ALIGN = 3,    /* K violates the per-type alignment rule */
     LB_ERR_VARIANT = 4,  /* variant outside LB_AUTO..8, or dtype unknown */
-    LB_ERR_OVERFLOW = 5, /* K is so large that an int32 sum could overflow */
+    LB_ERR_OVERFLOW = 5, /* K above the type's limit (int32 sum range; 1-bit: addressing) */
     LB_ERR_HIP = 6       /* the HIP runtime reported an error */
 } lb_status;
 
@@ -69,13 +69,15 @@ typedef enum { LB_S8 = 0, LB_S4 = 1, LB_B1 = 2 } lb_dtype;
 
 /* K limits: rows must be whole 16-byte chunks, and the worst-case |sum| must
  * fit int32 (16384 * K for int8; the int4 path accumulates 256 * a * b, the
- * same bound).  1-bit sums are at most K. */
+ * same bound).  1-bit sums are at most K, so the 1-bit limit comes instead from
+ * addressing: a workgroup tile spans up to 256 rows of K/8 bytes and its
+ * buffer offsets are 32-bit, so K/8 * 256 must stay below 2^32 (K < 2^27). */
 #define LB_S8_K_ALIGN 16
 #define LB_S4_K_ALIGN 32
 #define LB_B1_K_ALIGN 128
 #define LB_S8_K_MAX 131071
 #define LB_S4_K_MAX 131071
-#define LB_B1_K_MAX 2147483520 /* largest multiple of 128 below 2^31 */
+#define LB_B1_K_MAX 134217600 /* largest multiple of 128 below 2^27 */
 
 /*
  * C = A x B, int8 operands, int32 result.
@@ -121,6 +123,9 @@ int lb_gemm_s8_linear(const int8_t *X, const int8_t *W, const float *sx,
  *   or bits).  cu_count: compute units of the target GPU; <= 0 queries the
  *   current HIP device.  best: receives the chosen variant (0..8).  second:
  *   receives the runner-up, or may be NULL.
+ * By default the choice is the label of the nearest shape in a table of
+ * timings measured on MI355X; with the environment variable LB_SELECTOR=mlp
+ * the pages' feed-forward classifier (three hidden layers of 128) decides.
  * Host-only, microseconds, no GPU work.  Returns LB_ERR_NULL if best is NULL,
  * LB_ERR_SHAPE for non-positive sizes, LB_ERR_VARIANT for an unknown dtype and
  * LB_ERR_HIP if cu_count <= 0 and no device can be queried.
