@@ -40,12 +40,15 @@ __device__ inline i32x4 make_rsrc(const void *base, uint64_t num_records)
 // lane i's 16 bytes at rsrc.base + voff land at LDS byte lds_base + 16*i.  The
 // compiler does not see this LDS write (it would otherwise wait for every
 // outstanding copy before any LDS read, collapsing the pipeline); the kernels
-// order it explicitly with wait_vm_barrier().
+// order it explicitly with wait_vm_barrier().  On gfx9-family parts an LDS
+// copy must not read M0 in the instruction right after the SALU write that set
+// it, hence the s_nop between the two.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ inline void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_base)
 {
     asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
                  "buffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(lds_base)
