@@ -13,7 +13,8 @@ roofline of the GEMM kernel against MI355X's dense int8 MFMA peak, and the CPU
 oracle timed on a bounded sample of the same workload.  Extra fields report the
 int4 and int8 GEMMs at 4096^3, the 1-bit GEMM at 4096 x 4096 x 8192 bits and the
 int8 linear layer, each with its selected and default variants (kernel time from
-HIP-graph replays, so that host launch cost is excluded).
+HIP-graph replays, so that host launch cost is excluded), and, as context, the
+vendor library's int8 GEMM (hipBLASLt via torch._int_mm) at the same sizes.
 
 Usage: python bench.py [--gpus 1] [--steps 300] [--warmup 100]
 """
@@ -168,10 +169,29 @@ def measure(workload, torch, lb):
     ops = 2.0 * M * N * K
     peak = PEAK_VALU_B1_TOPS if dtype == "b1" else PEAK_INT8_TOPS
     tops = ops / t_sel / 1e12
-    return {"tops": round(tops, 2), "frac_of_peak": round(tops / peak, 4), "peak_tops": round(peak, 1),
-            "us_per_call": round(t_sel * 1e6, 2), "variant": sel,
-            "default_variant_us": round(t_def * 1e6, 2),
-            "speedup_vs_default": round(t_def / t_sel, 4)}
+    res = {"tops": round(tops, 2), "frac_of_peak": round(tops / peak, 4), "peak_tops": round(peak, 1),
+           "us_per_call": round(t_sel * 1e6, 2), "variant": sel,
+           "default_variant_us": round(t_def * 1e6, 2),
+           "speedup_vs_default": round(t_def / t_sel, 4)}
+    if dtype != "b1":
+        res.update(vendor_int8(M, N, K, torch, t_sel))
+    return res
+
+
+def vendor_int8(M, N, K, torch, t_ours):
+    """Context only: the vendor library's int8 GEMM (hipBLASLt behind
+    torch._int_mm) at the same M, N, K with the same operand layout (B stored
+    N x K).  It has no int4 path and no fused dequant, so for the int4 GEMM and
+    the linear layer this is the nearest library call, not the same operation."""
+    from bit_integer_gemm_amd.sweep import time_calls
+    try:
+        a = torch.randint(-128, 128, (M, K), dtype=torch.int8, device="cuda")
+        b = torch.randint(-128, 128, (N, K), dtype=torch.int8, device="cuda")
+        t, _ = time_calls(lambda: torch._int_mm(a, b.t()), torch, target_ms=30.0, groups=5, graph=False)
+    except Exception as e:  # the comparison is optional context
+        return {"vendor_int8_note": f"torch._int_mm unavailable: {type(e).__name__}"}
+    return {"vendor_int8_us": round(t * 1e6, 2), "vendor_int8_tops": round(2.0 * M * N * K / t / 1e12, 2),
+            "speedup_vs_vendor_int8": round(t / t_ours, 4)}
 
 
 def main():

@@ -1,4 +1,4 @@
-"""CPU oracle for the low-bit integer GEMM -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the low-bit integer GEMM and convolution -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The GPU library never calls it, and it
@@ -13,6 +13,8 @@ Layouts (readings; the pages fix only the product A x B = C and the bit widths):
   A  : M x K row-major            (int8 / packed int4 bytes / packed 1-bit words)
   B  : K x N column-major, i.e. an (N, K) row-major array of the same kind
   C  : M x N row-major int32
+Convolution (readings of the im2win convolution summary; see oracle.c):
+  x  : N x H x W x C (NHWC), f : Co x Kh x Kw x C, y : N x Ho x Wo x Co int32
 """
 from __future__ import annotations
 
@@ -50,6 +52,13 @@ def _bind(lib):
         f.restype = ctypes.c_int
     lib.orc_linear_s8.argtypes = [p, p, p, p, p, i64, i64, i64]
     lib.orc_linear_s8.restype = ctypes.c_int
+    conv_args = [p, p, p] + [i64] * 11
+    for name in ("orc_conv2d_s8", "orc_conv2d_s4", "orc_conv2d_im2win_s8"):
+        f = getattr(lib, name)
+        f.argtypes = conv_args
+        f.restype = ctypes.c_int
+    lib.orc_im2win_s8.argtypes = [p, p] + [i64] * 10
+    lib.orc_im2win_s8.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
     return lib
@@ -144,6 +153,86 @@ def linear_s8(X: np.ndarray, W: np.ndarray, sx: np.ndarray, sw: np.ndarray,
     if rc != 0:
         raise OracleOverflow("a sum of products does not fit int32")
     return out
+
+
+def conv_out_dims(H, W, Kh, Kw, stride=(1, 1), pad=(0, 0)):
+    """(Ho, Wo) of a convolution; ValueError for impossible geometry."""
+    sh, sw = stride
+    ph, pw = pad
+    if sh <= 0 or sw <= 0 or ph < 0 or pw < 0 or H + 2 * ph < Kh or W + 2 * pw < Kw:
+        raise ValueError("impossible convolution geometry")
+    return (H + 2 * ph - Kh) // sh + 1, (W + 2 * pw - Kw) // sw + 1
+
+
+def _conv_call(fn, X, F, C, stride, pad):
+    N, H, W = X.shape[:3]
+    Co, Kh, Kw = F.shape[:3]
+    Ho, Wo = conv_out_dims(H, W, Kh, Kw, stride, pad)
+    Y = np.empty((N, Ho, Wo, Co), np.int32)
+    rc = fn(_ptr(X), _ptr(F), _ptr(Y), N, H, W, C, Co, Kh, Kw, stride[0], stride[1], pad[0], pad[1])
+    if rc == 2:
+        raise ValueError("impossible convolution geometry")
+    if rc != 0:
+        raise OracleOverflow("a sum of products does not fit int32")
+    return Y
+
+
+def _check_conv(X, F, dtype, last):
+    for a, what in ((X, "X"), (F, "F")):
+        if a.dtype != dtype or a.ndim != 4 or not a.flags.c_contiguous or a.shape[3] != last:
+            raise ValueError(f"{what}: need a C-contiguous 4-D {np.dtype(dtype).name} array "
+                             f"with last dimension {last}, got {a.dtype} {a.shape}")
+
+
+def conv2d_s8(X: np.ndarray, F: np.ndarray, stride=(1, 1), pad=(0, 0), *, handle=None) -> np.ndarray:
+    """y (N, Ho, Wo, Co) int32 = convolution of x (N, H, W, C) int8 with f (Co, Kh, Kw, C) int8."""
+    L = handle or lib()
+    _check_conv(X, F, np.int8, X.shape[3] if X.ndim == 4 else -1)
+    return _conv_call(L.orc_conv2d_s8, X, F, X.shape[3], tuple(stride), tuple(pad))
+
+
+def conv2d_s4(X: np.ndarray, F: np.ndarray, C: int, stride=(1, 1), pad=(0, 0), *, handle=None) -> np.ndarray:
+    """Convolution of packed int4 x (N, H, W, C/2 bytes) with packed f (Co, Kh, Kw, C/2 bytes)."""
+    L = handle or lib()
+    if C <= 0 or C % 2:
+        raise ValueError("C must be a positive multiple of 2")
+    _check_conv(X, F, np.uint8, C // 2)
+    return _conv_call(L.orc_conv2d_s4, X, F, C, tuple(stride), tuple(pad))
+
+
+def im2win_s8(X: np.ndarray, Kh: int, Kw: int, stride=(1, 1), pad=(0, 0), *, handle=None) -> np.ndarray:
+    """The window tensor (N, Ho, W + 2 pw, Kh, C) of the im2win transformation."""
+    L = handle or lib()
+    if X.dtype != np.int8 or X.ndim != 4 or not X.flags.c_contiguous:
+        raise ValueError("X: need a C-contiguous 4-D int8 array")
+    N, H, W, C = X.shape
+    Ho, Wo = conv_out_dims(H, W, Kh, Kw, stride, pad)
+    Win = np.empty((N, Ho, W + 2 * pad[1], Kh, C), np.int8)
+    rc = L.orc_im2win_s8(_ptr(X), _ptr(Win), N, H, W, C, Kh, Kw, stride[0], stride[1], pad[0], pad[1])
+    if rc:
+        raise ValueError("impossible convolution geometry")
+    return Win
+
+
+def conv2d_im2win_s8(Win: np.ndarray, F: np.ndarray, H: int, W: int, stride=(1, 1), pad=(0, 0),
+                     *, handle=None) -> np.ndarray:
+    """Convolution taken from the window tensor, one contiguous window per output."""
+    L = handle or lib()
+    N, Ho, Wp, Kh, C = Win.shape
+    Co, Kh2, Kw, C2 = F.shape
+    if Win.dtype != np.int8 or F.dtype != np.int8 or Kh2 != Kh or C2 != C or Wp != W + 2 * pad[1]:
+        raise ValueError("window tensor and filter do not match")
+    if conv_out_dims(H, W, Kh, Kw, stride, pad)[0] != Ho:
+        raise ValueError("window tensor does not match the geometry")
+    Wo = conv_out_dims(H, W, Kh, Kw, stride, pad)[1]
+    Y = np.empty((N, Ho, Wo, Co), np.int32)
+    rc = L.orc_conv2d_im2win_s8(_ptr(np.ascontiguousarray(Win)), _ptr(np.ascontiguousarray(F)), _ptr(Y),
+                                N, H, W, C, Co, Kh, Kw, stride[0], stride[1], pad[0], pad[1])
+    if rc == 2:
+        raise ValueError("impossible convolution geometry")
+    if rc:
+        raise OracleOverflow("a sum of products does not fit int32")
+    return Y
 
 
 def num_threads(*, handle=None) -> int:

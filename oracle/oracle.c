@@ -29,7 +29,9 @@
  *
  * Every function returns 0 on success and 1 if some exact sum falls outside
  * int32 (the result buffer then holds the low 32 bits of those sums, and the
- * caller must treat it as invalid).  Shapes must be positive; K must be a
+ * caller must treat it as invalid); the convolutions return 2 for impossible
+ * geometry (non-positive stride, negative padding, window wider than the
+ * padded image).  Shapes must be positive; K must be a
  * multiple of 2 (int4) or 32 (1-bit) so that rows hold whole bytes / words.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no intrinsics, no
@@ -141,6 +143,157 @@ int orc_linear_s8(const int8_t *X, const int8_t *W, const float *sx,
             out[m * N + n] = (double)acc * (double)sx[m] * (double)sw[n];
         }
     }
+    return bad;
+}
+
+/* ---- 2-D convolution ------------------------------------------------------
+ *
+ * The im2win convolution summary (gist.science paper 2608.20725, "method":
+ * data transformation, NHWC layout, whole-batch execution) treats the
+ * convolution layer of a deep network: a window slides over each image and the
+ * values under it are multiplied with a filter and summed.  The page fixes no
+ * formula; the readings here (listed in the design notes) are the plain
+ * deep-learning convolution, i.e. cross-correlation without flipping:
+ *   x : N x H x W x C (NHWC)          f : Co x Kh x Kw x C (channels innermost)
+ *   y : N x Ho x Wo x Co int32 (NHWC), Ho = (H + 2 ph - Kh) / sh + 1,
+ *                                      Wo = (W + 2 pw - Kw) / sw + 1
+ *   y[n,ho,wo,co] = sum over kh, kw, c of
+ *                   x[n, ho*sh + kh - ph, wo*sw + kw - pw, c] * f[co, kh, kw, c]
+ * with x taken as 0 outside the image (zero padding).  No dilation, groups or
+ * bias.  The int4 variant packs two values per byte along C (even c in the low
+ * nibble), for the image and the filter alike.
+ *
+ * orc_conv2d_* is that definition written out.  orc_im2win_s8 and
+ * orc_conv2d_im2win_s8 follow the page's method instead: build the window
+ * tensor, then take each output as one contiguous dot product.  The tests
+ * require the two routes to agree. */
+
+/* Element c of the pixel (n, h, w), or 0 outside the image. */
+static int x8_at(const int8_t *X, int64_t H, int64_t W, int64_t C,
+                 int64_t n, int64_t h, int64_t w, int64_t c)
+{
+    if (h < 0 || h >= H || w < 0 || w >= W) return 0;
+    return s8_at(X + ((n * H + h) * W + w) * C, c);
+}
+
+static int x4_at(const uint8_t *X, int64_t H, int64_t W, int64_t C,
+                 int64_t n, int64_t h, int64_t w, int64_t c)
+{
+    if (h < 0 || h >= H || w < 0 || w >= W) return 0;
+    return s4_at(X + ((n * H + h) * W + w) * (C / 2), c);
+}
+
+static int conv_dims(int64_t H, int64_t W, int64_t Kh, int64_t Kw, int64_t sh,
+                     int64_t sw, int64_t ph, int64_t pw, int64_t *Ho, int64_t *Wo)
+{
+    if (sh <= 0 || sw <= 0 || ph < 0 || pw < 0) return 1;
+    if (H + 2 * ph < Kh || W + 2 * pw < Kw) return 1;
+    *Ho = (H + 2 * ph - Kh) / sh + 1;
+    *Wo = (W + 2 * pw - Kw) / sw + 1;
+    return 0;
+}
+
+int orc_conv2d_s8(const int8_t *X, const int8_t *F, int32_t *Y, int64_t N, int64_t H,
+                  int64_t W, int64_t C, int64_t Co, int64_t Kh, int64_t Kw, int64_t sh,
+                  int64_t sw, int64_t ph, int64_t pw)
+{
+    int64_t Ho, Wo;
+    if (conv_dims(H, W, Kh, Kw, sh, sw, ph, pw, &Ho, &Wo)) return 2;
+    int bad = 0;
+    int64_t q;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (q = 0; q < N * Ho; ++q) {
+        const int64_t n = q / Ho, ho = q % Ho;
+        for (int64_t wo = 0; wo < Wo; ++wo)
+            for (int64_t co = 0; co < Co; ++co) {
+                int64_t acc = 0;
+                for (int64_t kh = 0; kh < Kh; ++kh)
+                    for (int64_t kw = 0; kw < Kw; ++kw)
+                        for (int64_t c = 0; c < C; ++c)
+                            acc += (int64_t)x8_at(X, H, W, C, n, ho * sh + kh - ph, wo * sw + kw - pw, c) *
+                                   (int64_t)s8_at(F + ((co * Kh + kh) * Kw + kw) * C, c);
+                if (!fits_i32(acc)) bad = 1;
+                Y[((n * Ho + ho) * Wo + wo) * Co + co] = (int32_t)(uint32_t)(uint64_t)acc;
+            }
+    }
+    return bad;
+}
+
+int orc_conv2d_s4(const uint8_t *X, const uint8_t *F, int32_t *Y, int64_t N, int64_t H,
+                  int64_t W, int64_t C, int64_t Co, int64_t Kh, int64_t Kw, int64_t sh,
+                  int64_t sw, int64_t ph, int64_t pw)
+{
+    int64_t Ho, Wo;
+    if (C % 2 || conv_dims(H, W, Kh, Kw, sh, sw, ph, pw, &Ho, &Wo)) return 2;
+    int bad = 0;
+    int64_t q;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (q = 0; q < N * Ho; ++q) {
+        const int64_t n = q / Ho, ho = q % Ho;
+        for (int64_t wo = 0; wo < Wo; ++wo)
+            for (int64_t co = 0; co < Co; ++co) {
+                int64_t acc = 0;
+                for (int64_t kh = 0; kh < Kh; ++kh)
+                    for (int64_t kw = 0; kw < Kw; ++kw)
+                        for (int64_t c = 0; c < C; ++c)
+                            acc += (int64_t)x4_at(X, H, W, C, n, ho * sh + kh - ph, wo * sw + kw - pw, c) *
+                                   (int64_t)s4_at(F + ((co * Kh + kh) * Kw + kw) * (C / 2), c);
+                if (!fits_i32(acc)) bad = 1;
+                Y[((n * Ho + ho) * Wo + wo) * Co + co] = (int32_t)(uint32_t)(uint64_t)acc;
+            }
+    }
+    return bad;
+}
+
+/* The window tensor of the page's data transformation.  For each image n and
+ * output row ho, the Kh input rows that row ho reads are interleaved so that
+ * every padded column w holds its Kh x C values next to each other:
+ *   win[(((n*Ho + ho)*Wp + w)*Kh + kh)*C + c] = x[n, ho*sh + kh - ph, w - pw, c],
+ * Wp = W + 2 pw.  Rows that windows of different outputs share are stored once
+ * per output row, not once per output. */
+int orc_im2win_s8(const int8_t *X, int8_t *Win, int64_t N, int64_t H, int64_t W, int64_t C,
+                  int64_t Kh, int64_t Kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw)
+{
+    int64_t Ho, Wo;
+    if (conv_dims(H, W, Kh, Kw, sh, sw, ph, pw, &Ho, &Wo)) return 2;
+    const int64_t Wp = W + 2 * pw;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t ho = 0; ho < Ho; ++ho)
+            for (int64_t w = 0; w < Wp; ++w)
+                for (int64_t kh = 0; kh < Kh; ++kh)
+                    for (int64_t c = 0; c < C; ++c)
+                        Win[(((n * Ho + ho) * Wp + w) * Kh + kh) * C + c] =
+                            (int8_t)x8_at(X, H, W, C, n, ho * sh + kh - ph, w - pw, c);
+    return 0;
+}
+
+/* Output (n, ho, wo) from the window tensor: its window is the contiguous run
+ * of Kw*Kh*C values that starts at column w = wo*sw of row (n, ho), ordered
+ * (kw, kh, c); the filter value for run position t is f[co, kh, kw, c]. */
+int orc_conv2d_im2win_s8(const int8_t *Win, const int8_t *F, int32_t *Y, int64_t N, int64_t H,
+                         int64_t W, int64_t C, int64_t Co, int64_t Kh, int64_t Kw, int64_t sh,
+                         int64_t sw, int64_t ph, int64_t pw)
+{
+    int64_t Ho, Wo;
+    if (conv_dims(H, W, Kh, Kw, sh, sw, ph, pw, &Ho, &Wo)) return 2;
+    const int64_t Wp = W + 2 * pw, run = Kw * Kh * C;
+    int bad = 0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t ho = 0; ho < Ho; ++ho) {
+            const int8_t *row = Win + (n * Ho + ho) * Wp * Kh * C;
+            for (int64_t wo = 0; wo < Wo; ++wo) {
+                const int8_t *window = row + wo * sw * Kh * C;
+                for (int64_t co = 0; co < Co; ++co) {
+                    int64_t acc = 0;
+                    for (int64_t t = 0; t < run; ++t) {
+                        const int64_t kw = t / (Kh * C), kh = (t / C) % Kh, c = t % C;
+                        acc += (int64_t)window[t] * (int64_t)F[((co * Kh + kh) * Kw + kw) * C + c];
+                    }
+                    if (!fits_i32(acc)) bad = 1;
+                    Y[((n * Ho + ho) * Wo + wo) * Co + co] = (int32_t)(uint32_t)(uint64_t)acc;
+                }
+            }
+        }
     return bad;
 }
 

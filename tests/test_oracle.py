@@ -6,9 +6,12 @@ CUTLASS GEMM Optimization via Neural Networks", Research results item 1 and the
 editor's summary).  They print no worked example, so each pin below is one of:
 hand-worked fixtures (tests/golden), exhaustive tables built from Python
 integers, closed forms, algebraic identities, an independent numpy formulation,
-or a statistical property of the seeded inputs.  The final test plants plausible
-mistakes in a copy of the oracle's C source and checks that some pin catches
-each one.
+or a statistical property of the seeded inputs.  The convolution of the im2win
+convolution summary (gist.science paper 2608.20725, method section) is pinned
+the same way, plus two routes that do not go through its loops: a 1x1
+convolution is a GEMM, and the page's own window-tensor route must agree with
+the definition.  The final test plants plausible mistakes in a copy of the
+oracle's C source and checks that some pin catches each one.
 """
 import json
 import os
@@ -21,6 +24,7 @@ import inputs
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+GOLDEN_CONV = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_conv.json")
 
 
 # --------------------------------------------------------------------------
@@ -262,9 +266,123 @@ def pin_b1_statistics(h):
     assert 0.85 < C.std() / np.sqrt(3 * K / 16) < 1.15
 
 
+# --------------------------------------------------------------------------
+# convolution pins
+# --------------------------------------------------------------------------
+
+def conv_numpy(x, f, stride, pad):
+    """Independent formulation: zero-pad, take every window with numpy strides,
+    contract over (kh, kw, c) in int64.  x (N,H,W,C), f (Co,Kh,Kw,C) int64."""
+    N, H, W, C = x.shape
+    Co, Kh, Kw, _ = f.shape
+    (sh, sw), (ph, pw) = stride, pad
+    xp = np.pad(x, ((0, 0), (ph, ph), (pw, pw), (0, 0)))
+    win = np.lib.stride_tricks.sliding_window_view(xp, (Kh, Kw), axis=(1, 2))  # N,Hp-Kh+1,Wp-Kw+1,C,Kh,Kw
+    win = win[:, ::sh, ::sw]
+    return np.einsum("nhwcij,oijc->nhwo", win.astype(np.int64), f.astype(np.int64))
+
+
+def unpack_s4_last(packed):
+    """(..., C/2) packed bytes -> (..., C) int64 values (even c in the low nibble)."""
+    flat = packed.reshape(-1, packed.shape[-1])
+    return unpack_s4_np(flat).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+
+
+def pin_conv_golden(h):
+    with open(GOLDEN_CONV) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        if c["kind"] == "s8":
+            y = oracle.conv2d_s8(np.array(c["x"], np.int8), np.array(c["f"], np.int8),
+                                 c["stride"], c["pad"], handle=h)
+        else:
+            y = oracle.conv2d_s4(np.array(c["x_bytes"], np.uint8), np.array(c["f_bytes"], np.uint8),
+                                 c["C"], c["stride"], c["pad"], handle=h)
+        np.testing.assert_array_equal(y, np.array(c["y"], np.int32), err_msg=c["why"])
+
+
+def pin_conv_1x1_is_gemm(h):
+    """A 1x1 convolution with unit stride and no padding is the GEMM of the
+    pixels (N*H*W rows of C) with the filters (Co rows of C)."""
+    g = inputs.rng(41)
+    x = g.integers(-128, 128, (2, 5, 7, 48), dtype=np.int8)
+    f = g.integers(-128, 128, (9, 1, 1, 48), dtype=np.int8)
+    y = oracle.conv2d_s8(x, f, handle=h)
+    want = oracle.gemm_s8(x.reshape(-1, 48), f.reshape(9, 48), handle=h)
+    np.testing.assert_array_equal(y.reshape(-1, 9), want)
+    x4 = inputs.s4_rows(2 * 5 * 7, 64, 42).reshape(2, 5, 7, 32)
+    f4 = inputs.s4_rows(6, 64, 43).reshape(6, 1, 1, 32)
+    y4 = oracle.conv2d_s4(x4, f4, 64, handle=h)
+    want4 = oracle.gemm_s4(x4.reshape(-1, 32), f4.reshape(6, 32), 64, handle=h)
+    np.testing.assert_array_equal(y4.reshape(-1, 6), want4)
+
+
+CONV_CASES = [  # (N, H, W, C, Co, Kh, Kw, stride, pad)
+    (1, 6, 5, 3, 4, 3, 3, (1, 1), (1, 1)),
+    (2, 7, 9, 4, 3, 3, 2, (2, 1), (0, 1)),
+    (1, 9, 8, 2, 2, 5, 3, (2, 3), (2, 1)),
+    (3, 4, 4, 6, 5, 1, 3, (1, 2), (0, 2)),
+    (1, 3, 11, 8, 2, 3, 7, (1, 1), (1, 3)),
+]
+
+
+def pin_conv_numpy(h):
+    """Random convolutions (strides, paddings, non-square filters) against numpy."""
+    g = inputs.rng(44)
+    for (N, H, W, C, Co, Kh, Kw, st, pd) in CONV_CASES:
+        x = g.integers(-128, 128, (N, H, W, C), dtype=np.int8)
+        f = g.integers(-128, 128, (Co, Kh, Kw, C), dtype=np.int8)
+        np.testing.assert_array_equal(oracle.conv2d_s8(x, f, st, pd, handle=h), conv_numpy(x, f, st, pd))
+        C4 = 2 * C
+        x4 = inputs.s4_rows(N * H * W, C4, 45).reshape(N, H, W, C)
+        f4 = inputs.s4_rows(Co * Kh * Kw, C4, 46).reshape(Co, Kh, Kw, C)
+        want = conv_numpy(unpack_s4_last(x4), unpack_s4_last(f4), st, pd)
+        np.testing.assert_array_equal(oracle.conv2d_s4(x4, f4, C4, st, pd, handle=h), want)
+
+
+def pin_conv_closed_forms(h):
+    """Constant image and filter: each output is a*b*C times the number of
+    filter taps that land inside the image, counted per axis from the window
+    origin (ho*sh - ph, wo*sw - pw)."""
+    N, H, W, C, Co = 1, 7, 6, 5, 2
+    for (Kh, Kw, st, pd) in [(3, 3, (1, 1), (1, 1)), (5, 2, (2, 3), (2, 1)), (4, 4, (3, 1), (3, 0))]:
+        Ho, Wo = oracle.conv_out_dims(H, W, Kh, Kw, st, pd)
+        rows = [min(H, ho * st[0] - pd[0] + Kh) - max(0, ho * st[0] - pd[0]) for ho in range(Ho)]
+        cols = [min(W, wo * st[1] - pd[1] + Kw) - max(0, wo * st[1] - pd[1]) for wo in range(Wo)]
+        taps = np.array([[r * c for c in cols] for r in rows], np.int64)
+        for a, b in [(1, 1), (-128, -128), (127, -3)]:
+            y = oracle.conv2d_s8(np.full((N, H, W, C), a, np.int8), np.full((Co, Kh, Kw, C), b, np.int8),
+                                 st, pd, handle=h)
+            assert (y == (a * b * C * taps)[None, :, :, None]).all(), (Kh, Kw, st, pd, a, b)
+        C4 = 2 * C
+        for a, b in [(-8, -8), (7, -8)]:
+            x4 = inputs.pack_s4(np.full((N * H * W, C4), a, np.int8)).reshape(N, H, W, C)
+            f4 = inputs.pack_s4(np.full((Co * Kh * Kw, C4), b, np.int8)).reshape(Co, Kh, Kw, C)
+            y = oracle.conv2d_s4(x4, f4, C4, st, pd, handle=h)
+            assert (y == (a * b * C4 * taps)[None, :, :, None]).all(), (Kh, Kw, st, pd, a, b)
+
+
+def pin_conv_im2win_route(h):
+    """The page's window-tensor route (transform, then one contiguous dot product
+    per output) equals the definition, and the window tensor holds Kh/sh times
+    the image rather than im2col's Kh*Kw/(sh*sw) copies."""
+    g = inputs.rng(47)
+    for (N, H, W, C, Co, Kh, Kw, st, pd) in CONV_CASES:
+        x = g.integers(-128, 128, (N, H, W, C), dtype=np.int8)
+        f = g.integers(-128, 128, (Co, Kh, Kw, C), dtype=np.int8)
+        win = oracle.im2win_s8(x, Kh, Kw, st, pd, handle=h)
+        Ho, _ = oracle.conv_out_dims(H, W, Kh, Kw, st, pd)
+        assert win.shape == (N, Ho, W + 2 * pd[1], Kh, C)
+        y = oracle.conv2d_im2win_s8(win, f, H, W, st, pd, handle=h)
+        np.testing.assert_array_equal(y, oracle.conv2d_s8(x, f, st, pd, handle=h))
+        np.testing.assert_array_equal(y, conv_numpy(x, f, st, pd))
+
+
 PINS = [pin_golden, pin_s8_multiplication_table, pin_s4_decode_table, pin_b1_popcount_form,
         pin_small_random_python, pin_closed_forms, pin_identity, pin_transpose_identity,
-        pin_numpy_independent, pin_linear, pin_overflow_detected, pin_b1_statistics]
+        pin_numpy_independent, pin_linear, pin_overflow_detected, pin_b1_statistics,
+        pin_conv_golden, pin_conv_1x1_is_gemm, pin_conv_numpy, pin_conv_closed_forms,
+        pin_conv_im2win_route]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -321,6 +439,18 @@ MUTANTS = {
                            "const int8_t *brow = B + n;\n            int64_t acc = 0;\n            for (int64_t k = 0; k < K; ++k)\n                acc += (int64_t)s8_at(arow"),
     "linear_drops_sw": ("* (double)sx[m] * (double)sw[n];", "* (double)sx[m];"),
     "linear_sx_by_column": ("* (double)sx[m] * (double)sw[n];", "* (double)sx[n % M] * (double)sw[n];"),
+    "conv_pad_sign": ("x8_at(X, H, W, C, n, ho * sh + kh - ph, wo", "x8_at(X, H, W, C, n, ho * sh + kh + ph, wo"),
+    "conv_width_stride_ignored": ("ho * sh + kh - ph, wo * sw + kw - pw, c) *\n                                   (int64_t)s8_at",
+                                  "ho * sh + kh - ph, wo + kw - pw, c) *\n                                   (int64_t)s8_at"),
+    "conv_filter_kh_kw_swapped": ("(int64_t)s8_at(F + ((co * Kh + kh) * Kw + kw) * C, c);",
+                                  "(int64_t)s8_at(F + ((co * Kw + kw) * Kh + kh) * C, c);"),
+    "conv_padding_reads_one": ("if (h < 0 || h >= H || w < 0 || w >= W) return 0;\n    return s8_at",
+                               "if (h < 0 || h >= H || w < 0 || w >= W) return 1;\n    return s8_at"),
+    "conv_s4_filter_nibbles_swapped": ("(int64_t)s4_at(F + ((co * Kh + kh) * Kw + kw) * (C / 2), c);",
+                                       "(int64_t)s4_at(F + ((co * Kh + kh) * Kw + kw) * (C / 2), c ^ 1);"),
+    "conv_output_nchw": ("Y[((n * Ho + ho) * Wo + wo) * Co + co] = (int32_t)(uint32_t)(uint64_t)acc;\n            }\n    }\n    return bad;\n}\n\nint orc_conv2d_s4",
+                         "Y[((n * Co + co) * Ho + ho) * Wo + wo] = (int32_t)(uint32_t)(uint64_t)acc;\n            }\n    }\n    return bad;\n}\n\nint orc_conv2d_s4"),
+    "im2win_window_ignores_stride": ("const int8_t *window = row + wo * sw * Kh * C;", "const int8_t *window = row + wo * Kh * C;"),
     "overflow_unchecked": ("static int fits_i32(int64_t v) { return v >= INT32_MIN && v <= INT32_MAX; }",
                            "static int fits_i32(int64_t v) { (void)v; return 1; }"),
 }
