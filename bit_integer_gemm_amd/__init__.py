@@ -12,7 +12,9 @@ Operand conventions (see the header): A is (M, K) row-major, B is given as its
 (N, K) row-major rows (a column-major K x N matrix), C is (M, N) int32.  int4
 operands are (rows, K/2) uint8 with the even k in the low nibble; 1-bit
 operands are (rows, K/32) 32-bit words (torch.int32 or torch.uint32 bit
-patterns) with element k in bit k % 32 of word k // 32.
+patterns) with element k in bit k % 32 of word k // 32.  Convolutions take an
+NHWC image X (N, H, W, C), filters F (Co, Kh, Kw, C) and write Y (N, Ho, Wo,
+Co) int32; int4 tensors hold C/2 bytes in the last dimension.
 """
 from __future__ import annotations
 
@@ -29,10 +31,11 @@ LB_NUM_VARIANTS = 9
 LB_DEFAULT_VARIANT = 7
 K_ALIGN = {LB_S8: 16, LB_S4: 32, LB_B1: 128}
 K_MAX = {LB_S8: 131071, LB_S4: 131071, LB_B1: 134217600}
+CONV_C_ALIGN = {LB_S8: 64, LB_S4: 128}
 
 # Exported symbols of include/lb_gemm.h (checked by the CPU tests).
-EXPORTS = ("lb_gemm_s8", "lb_gemm_s4", "lb_gemm_b1", "lb_gemm_s8_linear",
-           "lb_select_variant", "lb_status_string", "lb_variant_info")
+EXPORTS = ("lb_gemm_s8", "lb_gemm_s4", "lb_gemm_b1", "lb_gemm_s8_linear", "lb_conv2d_s8",
+           "lb_conv2d_s4", "lb_select_variant", "lb_status_string", "lb_variant_info")
 
 
 class LbError(RuntimeError):
@@ -59,6 +62,10 @@ def load(path: str = LIB_PATH):
         f.restype = i32
     lib.lb_gemm_s8_linear.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
     lib.lb_gemm_s8_linear.restype = i32
+    for name in ("lb_conv2d_s8", "lb_conv2d_s4"):
+        f = getattr(lib, name)
+        f.argtypes = [p, p, p] + [i64] * 11 + [i32, p]
+        f.restype = i32
     ip = ctypes.POINTER(ctypes.c_int)
     lib.lb_select_variant.argtypes = [i32, i64, i64, i64, i32, ip, ip]
     lib.lb_select_variant.restype = i32
@@ -171,6 +178,37 @@ def lb_gemm_s8_linear(X, W, sx, sw, out, variant: int = LB_AUTO, stream=None) ->
     _raise(load().lb_gemm_s8_linear(_ptr(X), _ptr(W), _ptr(sx), _ptr(sw), _ptr(out), M, N, K, variant,
                                     _stream_handle(stream, _same_device(X, W, sx, sw, out))),
            "lb_gemm_s8_linear")
+
+
+def conv_out_dims(H: int, W: int, Kh: int, Kw: int, stride=(1, 1), pad=(0, 0)):
+    """(Ho, Wo) of a convolution (the formula in the header)."""
+    return (H + 2 * pad[0] - Kh) // stride[0] + 1, (W + 2 * pad[1] - Kw) // stride[1] + 1
+
+
+def _conv(name, dtype, X, F, Y, stride, pad, variant, stream, cdiv):
+    N, H, W, cl = X.shape
+    Co, Kh, Kw, cl2 = F.shape
+    C = cl * cdiv
+    Ho, Wo = conv_out_dims(H, W, Kh, Kw, stride, pad)
+    _check(X, (dtype,), (N, H, W, cl), "X")
+    _check(F, (dtype,), (Co, Kh, Kw, cl), "F")
+    import torch
+    _check(Y, (torch.int32,), (N, Ho, Wo, Co), "Y")
+    fn = getattr(load(), name)
+    _raise(fn(_ptr(X), _ptr(F), _ptr(Y), N, H, W, C, Co, Kh, Kw, stride[0], stride[1], pad[0], pad[1],
+              variant, _stream_handle(stream, _same_device(X, F, Y))), name)
+
+
+def lb_conv2d_s8(X, F, Y, stride=(1, 1), pad=(0, 0), variant: int = LB_AUTO, stream=None) -> None:
+    """Y (N, Ho, Wo, Co) int32 = convolution of X (N, H, W, C) int8 with F (Co, Kh, Kw, C) int8."""
+    import torch
+    _conv("lb_conv2d_s8", torch.int8, X, F, Y, tuple(stride), tuple(pad), variant, stream, 1)
+
+
+def lb_conv2d_s4(X, F, Y, stride=(1, 1), pad=(0, 0), variant: int = LB_AUTO, stream=None) -> None:
+    """As lb_conv2d_s8 for packed int4: X (N, H, W, C/2) uint8, F (Co, Kh, Kw, C/2) uint8."""
+    import torch
+    _conv("lb_conv2d_s4", torch.uint8, X, F, Y, tuple(stride), tuple(pad), variant, stream, 2)
 
 
 def lb_select_variant(dtype: int, M: int, N: int, K: int, cu_count: int = 0):

@@ -75,6 +75,67 @@ int lb_gemm_s8_linear(const int8_t *X, const int8_t *W, const float *sx, const f
                                   (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared checks and launch of the two convolutions.  cbytes_per_c2 is 2 for
+// int8 (bytes per pixel = C) and 1 for int4 (C/2); calign is the channel rule.
+int conv_entry(int kind, int dtype, const void *X, const void *F, int32_t *Y, int64_t N, int64_t H,
+               int64_t W, int64_t C, int64_t Co, int64_t Kh, int64_t Kw, int64_t sh, int64_t sw,
+               int64_t ph, int64_t pw, int variant, void *stream, int64_t calign, int64_t kmax)
+{
+    if (!X || !F || !Y) return LB_ERR_NULL;
+    if (N <= 0 || H <= 0 || W <= 0 || C <= 0 || Co <= 0 || Kh <= 0 || Kw <= 0 || sh <= 0 ||
+        sw <= 0 || ph < 0 || pw < 0)
+        return LB_ERR_SHAPE;
+    const int64_t lim = 0x7FFFFFFF;
+    if (H > lim || W > lim || C > lim || Co > lim || Kh > lim || Kw > lim || sh > lim ||
+        sw > lim || ph > lim || pw > lim)
+        return LB_ERR_SHAPE;
+    if (H + 2 * ph < Kh || W + 2 * pw < Kw) return LB_ERR_SHAPE;
+    if (C % calign != 0) return LB_ERR_ALIGN;
+    if (variant < LB_AUTO || variant >= LB_NUM_VARIANTS) return LB_ERR_VARIANT;
+    const int64_t Ho = (H + 2 * ph - Kh) / sh + 1, Wo = (W + 2 * pw - Kw) / sw + 1;
+    const int64_t cb = kind == lb::KIND_S8 ? C : C / 2;
+    const int64_t K = Kh * Kw * C;  // elements per window
+    if (K > kmax) return LB_ERR_OVERFLOW;
+    // 32-bit byte offsets reach every pixel of the padded image and every output row.
+    const double padded = (double)N * (double)(H + 2 * ph) * (double)(W + 2 * pw) * (double)cb;
+    if (padded >= 2147483648.0 || (double)N * (double)Ho * (double)Wo >= 2147483648.0)
+        return LB_ERR_OVERFLOW;
+    const int64_t M = N * Ho * Wo, Kb = Kh * Kw * cb;
+    int v = variant;
+    if (v == LB_AUTO && lb::select_from_table(dtype, M, Co, K, 0, &v, nullptr) != LB_OK)
+        v = LB_DEFAULT_VARIANT;
+    lb::ConvGeom g;
+    g.H = (int32_t)H; g.W = (int32_t)W; g.Cb = (int32_t)cb; g.Kh = (int32_t)Kh; g.Kw = (int32_t)Kw;
+    g.sh = (int32_t)sh; g.sw = (int32_t)sw; g.ph = (int32_t)ph; g.pw = (int32_t)pw;
+    g.Ho = (int32_t)Ho; g.Wo = (int32_t)Wo;
+    g.x_bytes = (uint32_t)(N * H * W * cb);
+    return finish(lb::launch_conv(kind, v, X, F, Y, M, Co, Kb, g, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int lb_conv2d_s8(const int8_t *X, const int8_t *F, int32_t *Y, int64_t N, int64_t H, int64_t W,
+                 int64_t C, int64_t Co, int64_t Kh, int64_t Kw, int64_t sh, int64_t sw, int64_t ph,
+                 int64_t pw, int variant, void *stream)
+{
+    return conv_entry(lb::KIND_S8, LB_S8, X, F, Y, N, H, W, C, Co, Kh, Kw, sh, sw, ph, pw, variant,
+                      stream, LB_CONV_S8_C_ALIGN, LB_S8_K_MAX);
+}
+
+int lb_conv2d_s4(const uint8_t *X, const uint8_t *F, int32_t *Y, int64_t N, int64_t H, int64_t W,
+                 int64_t C, int64_t Co, int64_t Kh, int64_t Kw, int64_t sh, int64_t sw, int64_t ph,
+                 int64_t pw, int variant, void *stream)
+{
+    return conv_entry(lb::KIND_S4, LB_S4, X, F, Y, N, H, W, C, Co, Kh, Kw, sh, sw, ph, pw, variant,
+                      stream, LB_CONV_S4_C_ALIGN, LB_S4_K_MAX);
+}
+
 int lb_select_variant(int dtype, int64_t M, int64_t N, int64_t K, int cu_count, int *best,
                       int *second)
 {

@@ -15,6 +15,18 @@ hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void
                        hipStream_t s);
 int mfma_variant_info(int variant, int *bm, int *bn, int *bk_bytes, int *stages);
 
+// Geometry of a convolution run as a GEMM whose A rows are gathered from an
+// NHWC image: output pixel r = (n*Ho + ho)*Wo + wo is row r, the filter taps
+// (kh, kw, channel byte) are the K axis.  Cb is bytes per pixel (C or C/2) and
+// a multiple of 64; x_bytes = N*H*W*Cb < 2^31.
+struct ConvGeom {
+    int32_t H, W, Cb, Kh, Kw, sh, sw, ph, pw, Ho, Wo;
+    uint32_t x_bytes;
+};
+// kind KIND_S8 or KIND_S4; M = N*Ho*Wo, N = Co, Kb = Kh*Kw*Cb.
+hipError_t launch_conv(int kind, int variant, const void *X, const void *F, int32_t *Y,
+                       int64_t M, int64_t N, int64_t Kb, const ConvGeom &g, hipStream_t s);
+
 // 1-bit VALU family.  Kw is the row length in 32-bit words (K/32).
 hipError_t launch_b1(int variant, const uint32_t *A, const uint32_t *B, int32_t *C, int64_t M,
                      int64_t N, int64_t Kw, hipStream_t s);

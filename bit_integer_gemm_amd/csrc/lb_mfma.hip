@@ -37,6 +37,15 @@
 //    exactly and an arithmetic shift by 8 recovers C.
 //  * Rows past M or N read as zero through the buffer range check; a partial
 //    last K stage has its out-of-range A pieces zeroed in LDS before use.
+//  * Convolution (the im2win convolution summary, gist.science paper
+//    2608.20725, method: NHWC images, a window per output) runs through the
+//    same kernel: row r of A is output pixel r and its K axis walks the filter
+//    taps (kh, kw) and the channels.  The page's window tensor is never built:
+//    each copy lane reads its 16-byte piece of the window straight from the
+//    NHWC image, the window tensor's addressing without its memory.  Channel
+//    bytes per pixel are a multiple of 64, so one 64-byte K block sits inside
+//    a single tap; pieces that fall in the zero padding (or past M or K) get
+//    an offset with bit 31 set, beyond the buffer range, and load zero.
 #include "lb_device.hpp"
 #include "lb_internal.hpp"
 
@@ -104,11 +113,11 @@ __device__ inline i32x4 mfma16(i32x4 a, i32x4 b, i32x4 c)
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-template <class C, int KIND>
+template <class C, int KIND, bool CONV>
 __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, void *__restrict__ out,
     const float *__restrict__ sx, const float *__restrict__ sw,
-    int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n)
+    int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n, ConvGeom g)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE_BYTES];
 
@@ -138,17 +147,72 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     }
     const uint32_t smem_base = lds_addr(smem);
 
+    // Convolution: per A copy, the window origin of its output pixel and the
+    // byte offset of that origin's channel piece (valid only inside the image).
+    int32_t cv_hi0[C::NDMA_A], cv_wi0[C::NDMA_A], cv_base[C::NDMA_A];
+    bool cv_row[C::NDMA_A];
+    int32_t cv_kh = 0, cv_kw = 0, cv_cb = 0;  // first K block of the next stage to copy
+    if constexpr (CONV) {
+        const int32_t hw = g.Ho * g.Wo;
+#pragma unroll
+        for (int i = 0; i < C::NDMA_A; ++i) {
+            const int j = (int)wave + C::NW * i;
+            const int32_t r = (int32_t)m0 + (j % (C::BM / 16)) * 16 + (int32_t)blk_row_of_lane(lane);
+            cv_row[i] = r < M;
+            const int32_t rr = cv_row[i] ? r : 0;
+            const int32_t n = rr / hw, rem = rr - n * hw;
+            const int32_t ho = rem / g.Wo, wo = rem - ho * g.Wo;
+            cv_hi0[i] = ho * g.sh - g.ph;
+            cv_wi0[i] = wo * g.sw - g.pw;
+            cv_base[i] = ((n * g.H + cv_hi0[i]) * g.W + cv_wi0[i]) * g.Cb +
+                         (int32_t)blk_chunk_of_lane(lane) * 16;
+        }
+    }
+    auto next_block = [&](int32_t &kh, int32_t &kw, int32_t &cb) {
+        cb += 64;
+        if (cb >= g.Cb) {
+            cb = 0;
+            if (++kw >= g.Kw) { kw = 0; ++kh; }
+        }
+    };
+
     auto issue = [&](int64_t kt, int slot) {
         const int64_t k0 = kt * C::BK;
-        const i32x4 ra = make_rsrc(Ab + k0, a_bytes > k0 ? (uint64_t)(a_bytes - k0) : 0);
+        i32x4 ra;
+        if constexpr (CONV) ra = make_rsrc(A, g.x_bytes);
+        else ra = make_rsrc(Ab + k0, a_bytes > k0 ? (uint64_t)(a_bytes - k0) : 0);
         const i32x4 rb = make_rsrc(Bb + k0, b_bytes > k0 ? (uint64_t)(b_bytes - k0) : 0);
+        // Filter tap and channel byte of each K block of this stage (stages are
+        // copied in order, one call per stage).
+        int32_t bkh[C::KB], bkw[C::KB], bcb[C::KB];
+        if constexpr (CONV) {
+#pragma unroll
+            for (int b = 0; b < C::KB; ++b) {
+                bkh[b] = cv_kh; bkw[b] = cv_kw; bcb[b] = cv_cb;
+                next_block(cv_kh, cv_kw, cv_cb);
+            }
+        }
         const uint32_t sbase = smem_base + slot * C::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::NDMA; ++i) {
             const bool isA = i < C::NDMA_A;
             const int j = (int)wave + C::NW * (isA ? i : i - C::NDMA_A);
             const uint32_t dst = sbase + (isA ? j : C::ABLK + j) * 1024;
-            dma16(isA ? ra : rb, voff[i], dst);
+            uint32_t vo = voff[i];
+            if constexpr (CONV) {
+                if (isA) {
+                    const int kb = j / (C::BM / 16);
+                    int32_t kh = bkh[0], kw = bkw[0], cb = bcb[0];
+#pragma unroll
+                    for (int b = 1; b < C::KB; ++b)
+                        if (kb == b) { kh = bkh[b]; kw = bkw[b]; cb = bcb[b]; }
+                    const int32_t hi = cv_hi0[i] + kh, wi = cv_wi0[i] + kw;
+                    const bool ok = cv_row[i] && kh < g.Kh && (uint32_t)hi < (uint32_t)g.H &&
+                                    (uint32_t)wi < (uint32_t)g.W;
+                    vo = ok ? (uint32_t)(cv_base[i] + (kh * g.W + kw) * g.Cb + cb) : 0x80000000u;
+                }
+            }
+            dma16(isA ? ra : rb, vo, dst);
         }
     };
 
@@ -268,16 +332,17 @@ using L2 = MfmaCfg<256, 256, 128, 4, 4, 2>;   // 128 KiB, 16 waves of 64x64
 using L3 = MfmaCfg<256, 256, 64, 4, 4, 3>;    // 96 KiB
 using L4 = MfmaCfg<256, 256, 64, 4, 4, 4>;    // 128 KiB
 
-template <class C, int KIND>
+template <class C, int KIND, bool CONV>
 static hipError_t launch_one(const void *A, const void *B, void *out, const float *sx,
-                             const float *sw, int64_t M, int64_t N, int64_t Kb, hipStream_t s)
+                             const float *sw, int64_t M, int64_t N, int64_t Kb, const ConvGeom &g,
+                             hipStream_t s)
 {
     const uint64_t tm = (uint64_t)((M + C::BM - 1) / C::BM);
     const uint64_t tn = (uint64_t)((N + C::BN - 1) / C::BN);
     if (tm * tn > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((mfma_gemm_kernel<C, KIND>), dim3((uint32_t)(tm * tn)), dim3(C::NT), 0, s,
-                       (const int8_t *)A, (const int8_t *)B, out, sx, sw, (int32_t)M, (int32_t)N,
-                       (int32_t)Kb, (uint32_t)tm, (uint32_t)tn);
+    hipLaunchKernelGGL((mfma_gemm_kernel<C, KIND, CONV>), dim3((uint32_t)(tm * tn)), dim3(C::NT), 0,
+                       s, (const int8_t *)A, (const int8_t *)B, out, sx, sw, (int32_t)M, (int32_t)N,
+                       (int32_t)Kb, (uint32_t)tm, (uint32_t)tn, g);
     return hipGetLastError();
 }
 
@@ -287,20 +352,21 @@ static void info_one(int *bm, int *bn, int *bk, int *st)
     *bm = C::BM; *bn = C::BN; *bk = C::BK; *st = C::ST;
 }
 
-template <int KIND>
+template <int KIND, bool CONV>
 static hipError_t dispatch(int variant, const void *A, const void *B, void *out, const float *sx,
-                           const float *sw, int64_t M, int64_t N, int64_t Kb, hipStream_t s)
+                           const float *sw, int64_t M, int64_t N, int64_t Kb, const ConvGeom &g,
+                           hipStream_t s)
 {
     switch (variant) {
-    case 0: return launch_one<S2, KIND>(A, B, out, sx, sw, M, N, Kb, s);
-    case 1: return launch_one<S3, KIND>(A, B, out, sx, sw, M, N, Kb, s);
-    case 2: return launch_one<S4, KIND>(A, B, out, sx, sw, M, N, Kb, s);
-    case 3: return launch_one<M2, KIND>(A, B, out, sx, sw, M, N, Kb, s);
-    case 4: return launch_one<M3, KIND>(A, B, out, sx, sw, M, N, Kb, s);
-    case 5: return launch_one<M4, KIND>(A, B, out, sx, sw, M, N, Kb, s);
-    case 6: return launch_one<L2, KIND>(A, B, out, sx, sw, M, N, Kb, s);
-    case 7: return launch_one<L3, KIND>(A, B, out, sx, sw, M, N, Kb, s);
-    case 8: return launch_one<L4, KIND>(A, B, out, sx, sw, M, N, Kb, s);
+    case 0: return launch_one<S2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 1: return launch_one<S3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 2: return launch_one<S4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 3: return launch_one<M2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 4: return launch_one<M3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 5: return launch_one<M4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 6: return launch_one<L2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 7: return launch_one<L3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 8: return launch_one<L4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -309,10 +375,22 @@ hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void
                        const float *sx, const float *sw, int64_t M, int64_t N, int64_t Kb,
                        hipStream_t s)
 {
+    const ConvGeom none{};
     switch (kind) {
-    case KIND_S8: return dispatch<KIND_S8>(variant, A, B, out, sx, sw, M, N, Kb, s);
-    case KIND_S4: return dispatch<KIND_S4>(variant, A, B, out, sx, sw, M, N, Kb, s);
-    case KIND_LINEAR: return dispatch<KIND_LINEAR>(variant, A, B, out, sx, sw, M, N, Kb, s);
+    case KIND_S8: return dispatch<KIND_S8, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
+    case KIND_S4: return dispatch<KIND_S4, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
+    case KIND_LINEAR:
+        return dispatch<KIND_LINEAR, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_conv(int kind, int variant, const void *X, const void *F, int32_t *Y,
+                       int64_t M, int64_t N, int64_t Kb, const ConvGeom &g, hipStream_t s)
+{
+    switch (kind) {
+    case KIND_S8: return dispatch<KIND_S8, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, g, s);
+    case KIND_S4: return dispatch<KIND_S4, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, g, s);
     default: return hipErrorInvalidValue;
     }
 }

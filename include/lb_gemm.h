@@ -116,6 +116,40 @@ int lb_gemm_s8_linear(const int8_t *X, const int8_t *W, const float *sx,
                       int64_t K, int variant, void *stream);
 
 /*
+ * Low-bit 2-D convolution over a batch of NHWC images (the im2win convolution
+ * summary, gist.science paper 2608.20725: problem statement and method, which
+ * treat the convolution layer over NHWC data for the whole batch at once).
+ * The page gives no formula; this is the plain deep-learning convolution
+ * (cross-correlation, zero padding, no dilation, groups or bias):
+ *   Ho = (H + 2*ph - Kh)/sh + 1,  Wo = (W + 2*pw - Kw)/sw + 1,
+ *   Y[((n*Ho + ho)*Wo + wo)*Co + co] = sum over kh < Kh, kw < Kw, c < C of
+ *       X[n, ho*sh + kh - ph, wo*sw + kw - pw, c] * F[co, kh, kw, c]
+ *   with X read as 0 outside the H x W image.
+ *   X: N x H x W x C (NHWC), F: Co x Kh x Kw x C (channels innermost, i.e. Co
+ *   rows of one window each), Y: N x Ho x Wo x Co int32 (NHWC).
+ * It runs as a GEMM with M = N*Ho*Wo, N = Co, K = Kh*Kw*C whose A rows (the
+ * page's windows) are read straight from X: no window or column buffer is
+ * allocated.  LB_AUTO picks the variant the GEMM of that shape would get.
+ * C must be a multiple of LB_CONV_S8_C_ALIGN (int8) or LB_CONV_S4_C_ALIGN
+ * (int4, packed two per byte along C, even c in the low nibble, for X and F
+ * alike), else LB_ERR_ALIGN.  LB_ERR_SHAPE for a non-positive size or stride,
+ * negative padding or a filter wider than the padded image; LB_ERR_OVERFLOW if
+ * Kh*Kw*C exceeds the type's K limit or the padded image or N*Ho*Wo reaches
+ * 2^31 (byte offsets are 32-bit).  Pointers, stream and errors otherwise as for
+ * the GEMMs.
+ */
+#define LB_CONV_S8_C_ALIGN 64
+#define LB_CONV_S4_C_ALIGN 128
+int lb_conv2d_s8(const int8_t *X, const int8_t *F, int32_t *Y, int64_t N,
+                 int64_t H, int64_t W, int64_t C, int64_t Co, int64_t Kh,
+                 int64_t Kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                 int variant, void *stream);
+int lb_conv2d_s4(const uint8_t *X, const uint8_t *F, int32_t *Y, int64_t N,
+                 int64_t H, int64_t W, int64_t C, int64_t Co, int64_t Kh,
+                 int64_t Kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                 int variant, void *stream);
+
+/*
  * Per-shape variant choice (Research results, items 2-3: the template index is
  * predicted from M, N, K and the GPU's multiprocessor count, and judged by
  * whether the true best template is among the top two).

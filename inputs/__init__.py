@@ -10,7 +10,8 @@ Formats (readings; the pages name 1-, 4- and 8-bit operands but no storage):
   int4  : signed nibbles in [-8, 7], two per byte along K, even k in the low nibble.
   1-bit : 32 elements per uint32 along K, element k in bit (k % 32) of word k // 32.
 Every operand is stored as rows of K elements: A as M rows, B as N rows (the
-bytes of a K x N column-major matrix).
+bytes of a K x N column-major matrix).  Convolution images are NHWC and filters
+(Co, Kh, Kw, C): the same rows, reshaped, with C as the packed axis.
 
 The distributions mirror the workloads the library is measured on: uniform int8
 over [-128, 127], uniform int4 over [-8, 7], Bernoulli(0.5) bits and fp32 scales
@@ -76,6 +77,16 @@ def b1_rows(rows: int, K: int, seed: int) -> np.ndarray:
     if K % 32:
         raise ValueError("K must be a multiple of 32")
     return rng(seed).integers(0, 2**32, size=(rows, K // 32), dtype=np.uint32)
+
+
+def s8_nhwc(N: int, H: int, W: int, C: int, seed: int) -> np.ndarray:
+    """(N, H, W, C) int8 image batch (or (Co, Kh, Kw, C) filters), uniform over [-128, 127]."""
+    return s8_rows(N * H * W, C, seed).reshape(N, H, W, C)
+
+
+def s4_nhwc(N: int, H: int, W: int, C: int, seed: int) -> np.ndarray:
+    """(N, H, W, C/2) packed int4 bytes along C, values uniform over [-8, 7]."""
+    return s4_rows(N * H * W, C, seed).reshape(N, H, W, C // 2)
 
 
 def scales(n: int, seed: int) -> np.ndarray:

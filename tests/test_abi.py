@@ -46,6 +46,8 @@ def test_header_constants_match_binding():
     assert define("LB_B1_K_ALIGN") == lb.K_ALIGN[lb.LB_B1]
     assert define("LB_S8_K_MAX") == lb.K_MAX[lb.LB_S8]
     assert define("LB_B1_K_MAX") == lb.K_MAX[lb.LB_B1]
+    assert define("LB_CONV_S8_C_ALIGN") == lb.CONV_C_ALIGN[lb.LB_S8]
+    assert define("LB_CONV_S4_C_ALIGN") == lb.CONV_C_ALIGN[lb.LB_S4]
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
@@ -77,6 +79,43 @@ def test_linear_argument_checks(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, 4, 4, 16, -1, NULL) == lb.LB_ERR_NULL
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 24, -1, NULL) == lb.LB_ERR_ALIGN
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 131072, -1, NULL) == lb.LB_ERR_OVERFLOW
+
+
+CONV_OK = dict(N=2, H=8, W=9, C=128, Co=16, Kh=3, Kw=3, sh=1, sw=1, ph=1, pw=1)
+
+
+def conv_args(**kw):
+    d = dict(CONV_OK, **kw)
+    return [d[k] for k in ("N", "H", "W", "C", "Co", "Kh", "Kw", "sh", "sw", "ph", "pw")]
+
+
+@pytest.mark.parametrize("fn,calign", [("lb_conv2d_s8", 64), ("lb_conv2d_s4", 128)])
+def test_conv_argument_checks(lib, fn, calign):
+    f = getattr(lib, fn)
+    assert f(NULL, FAKE, FAKE, *conv_args(), -1, NULL) == lb.LB_ERR_NULL
+    assert f(FAKE, NULL, FAKE, *conv_args(), -1, NULL) == lb.LB_ERR_NULL
+    assert f(FAKE, FAKE, NULL, *conv_args(), -1, NULL) == lb.LB_ERR_NULL
+    for bad in (dict(N=0), dict(H=-1), dict(C=0), dict(Co=0), dict(Kh=0), dict(sw=0), dict(sh=-2),
+                dict(ph=-1), dict(Kh=11), dict(Kw=12, pw=1), dict(H=2**31)):
+        assert f(FAKE, FAKE, FAKE, *conv_args(**bad), -1, NULL) == lb.LB_ERR_SHAPE, bad
+    assert f(FAKE, FAKE, FAKE, *conv_args(C=calign // 2), -1, NULL) == lb.LB_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, *conv_args(C=calign + 16), -1, NULL) == lb.LB_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, *conv_args(), 9, NULL) == lb.LB_ERR_VARIANT
+    assert f(FAKE, FAKE, FAKE, *conv_args(), -2, NULL) == lb.LB_ERR_VARIANT
+    # window longer than the exact-int32 K limit
+    assert f(FAKE, FAKE, FAKE, *conv_args(C=calign * 2048, Kh=1, Kw=1, ph=0, pw=0), 0, NULL) == lb.LB_ERR_OVERFLOW
+    # padded image of 2^31 bytes or more cannot be addressed with 32-bit offsets
+    big = dict(N=1024, H=256, W=256, C=calign * (1 if calign == 64 else 2), Kh=1, Kw=1, ph=0, pw=0)
+    assert f(FAKE, FAKE, FAKE, *conv_args(**big), 0, NULL) == lb.LB_ERR_OVERFLOW
+
+
+def test_conv_out_dims_formula():
+    assert lb.conv_out_dims(56, 56, 3, 3, (1, 1), (1, 1)) == (56, 56)
+    assert lb.conv_out_dims(28, 28, 3, 3, (2, 2), (1, 1)) == (14, 14)
+    assert lb.conv_out_dims(7, 9, 1, 7, (3, 2), (0, 3)) == (3, 5)
+    import oracle
+    for args in [(56, 56, 3, 3, (1, 1), (1, 1)), (11, 13, 5, 5, (2, 2), (2, 2)), (7, 9, 1, 7, (3, 2), (0, 3))]:
+        assert lb.conv_out_dims(*args) == oracle.conv_out_dims(*args)
 
 
 def test_overflow_bound_is_the_int32_limit():

@@ -1,0 +1,137 @@
+"""GPU parity of the low-bit convolution against the CPU oracle.
+
+The operation is the convolution of the im2win convolution summary
+(gist.science paper 2608.20725, problem statement and method: NHWC images, the
+whole batch at once) under the reading written in the oracle: zero padding,
+strides, filters (Co, Kh, Kw, C), output NHWC int32.  Every result is an
+integer sum and must match the oracle bit-exactly.
+
+The small cases run every kernel variant and cover ragged output-pixel counts
+and channel counts (not multiples of any tile), non-square filters, unequal
+strides and paddings, padding as wide as the filter (outputs that see only
+padding), a 1x1 filter with stride larger than one and a single-pixel image.
+The layer-sized cases run in the configuration the benchmark times (automatic
+variant choice) and are compared in full.  Outputs land in buffers with guard
+bands that must come back untouched.
+"""
+import numpy as np
+import pytest
+
+import inputs
+import oracle
+
+torch = pytest.importorskip("torch")
+import bit_integer_gemm_amd as lb  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+SENTINEL = 0x5A5A5A5A
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_conv(kind, x, f, stride, pad, variant):
+    N, H, W = x.shape[:3]
+    Co, Kh, Kw = f.shape[:3]
+    Ho, Wo = lb.conv_out_dims(H, W, Kh, Kw, stride, pad)
+    n = N * Ho * Wo * Co
+    flat = torch.full((n + 2 * GUARD,), SENTINEL, dtype=torch.int32, device="cuda")
+    Y = flat[GUARD:GUARD + n].view(N, Ho, Wo, Co)
+    if kind == "s8":
+        lb.lb_conv2d_s8(to_dev(x), to_dev(f), Y, stride, pad, variant)
+    else:
+        lb.lb_conv2d_s4(to_dev(x), to_dev(f), Y, stride, pad, variant)
+    torch.cuda.synchronize()
+    head, tail = flat[:GUARD].cpu(), flat[-GUARD:].cpu()
+    assert (head == SENTINEL).all() and (tail == SENTINEL).all(), "write outside Y"
+    return Y.cpu().numpy()
+
+
+def make(kind, N, H, W, C, Co, Kh, Kw, seed):
+    if kind == "s8":
+        return inputs.s8_nhwc(N, H, W, C, seed), inputs.s8_nhwc(Co, Kh, Kw, C, seed + 1)
+    return inputs.s4_nhwc(N, H, W, C, seed), inputs.s4_nhwc(Co, Kh, Kw, C, seed + 1)
+
+
+def ref(kind, x, f, C, stride, pad):
+    if kind == "s8":
+        return oracle.conv2d_s8(x, f, stride, pad)
+    return oracle.conv2d_s4(x, f, C, stride, pad)
+
+
+# (N, H, W, C, Co, Kh, Kw, stride, pad); C is in elements (multiple of 64 / 128)
+SMALL = [
+    (2, 9, 7, 128, 40, 3, 3, (1, 1), (1, 1)),
+    (1, 12, 10, 128, 72, 3, 2, (2, 1), (1, 0)),
+    (3, 5, 6, 256, 33, 1, 1, (1, 1), (0, 0)),
+    (1, 11, 13, 128, 17, 5, 5, (2, 2), (2, 2)),
+    (2, 4, 5, 128, 9, 3, 3, (1, 1), (3, 3)),      # padding wider than the filter reach
+    (1, 7, 9, 256, 24, 1, 1, (3, 2), (0, 0)),
+    (1, 1, 1, 128, 5, 1, 1, (1, 1), (0, 0)),      # a single pixel
+    (1, 6, 3, 128, 130, 1, 7, (1, 1), (0, 3)),    # 1 x 7 filter, Co over two medium tiles
+]
+
+
+def conv_c(kind, C):
+    """Channel count for the dtype: int8 cases halve C where it stays a multiple of 64."""
+    return C if kind == "s4" else max(64, C // 2)
+
+
+@pytest.mark.parametrize("kind", ["s8", "s4"])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_conv_small_all_variants(kind, case):
+    N, H, W, C, Co, Kh, Kw, st, pd = SMALL[case]
+    C = conv_c(kind, C)
+    x, f = make(kind, N, H, W, C, Co, Kh, Kw, 600 + 10 * case)
+    want = ref(kind, x, f, C, st, pd)
+    for v in [lb.LB_AUTO] + list(range(lb.LB_NUM_VARIANTS)):
+        got = run_conv(kind, x, f, st, pd, v)
+        np.testing.assert_array_equal(got, want, err_msg=f"{kind} case {case} variant {v}")
+
+
+@pytest.mark.parametrize("kind", ["s8", "s4"])
+def test_conv_1x1_matches_gemm_on_gpu(kind):
+    """A 1x1, stride-1, unpadded convolution is the GEMM of pixels with filters."""
+    N, H, W, C, Co = 2, 17, 15, 256, 96
+    x, f = make(kind, N, H, W, C, Co, 1, 1, 700)
+    y = run_conv(kind, x, f, (1, 1), (0, 0), lb.LB_AUTO)
+    dA = to_dev(x.reshape(N * H * W, -1))
+    dB = to_dev(f.reshape(Co, -1))
+    Cm = torch.empty((N * H * W, Co), dtype=torch.int32, device="cuda")
+    (lb.lb_gemm_s8 if kind == "s8" else lb.lb_gemm_s4)(dA, dB, Cm)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.reshape(-1, Co), Cm.cpu().numpy())
+
+
+# Layer-sized shapes (synthetic; see the design notes for the recipe).
+LAYERS = {
+    "3x3_s1_56x56x64": (8, 56, 56, 64, 64, 3, 3, (1, 1), (1, 1)),
+    "3x3_s2_28x28x128": (8, 28, 28, 128, 256, 3, 3, (2, 2), (1, 1)),
+    "1x1_14x14x256": (8, 14, 14, 256, 1024, 1, 1, (1, 1), (0, 0)),
+    "5x5_s1_14x14x128": (4, 14, 14, 128, 128, 5, 5, (1, 1), (2, 2)),
+}
+
+
+@pytest.mark.parametrize("kind", ["s8", "s4"])
+@pytest.mark.parametrize("name", sorted(LAYERS))
+def test_conv_layer_full_compare(kind, name):
+    N, H, W, C, Co, Kh, Kw, st, pd = LAYERS[name]
+    if kind == "s4" and C % 128:
+        C *= 2
+    x, f = make(kind, N, H, W, C, Co, Kh, Kw, 800)
+    want = ref(kind, x, f, C, st, pd)
+    got = run_conv(kind, x, f, st, pd, lb.LB_AUTO)
+    np.testing.assert_array_equal(got, want, err_msg=f"{kind} {name}")
+
+
+def test_conv_extreme_values():
+    """All -128 operands with padding: every output is 16384*C times its in-image tap count."""
+    N, H, W, C, Co, Kh, Kw, st, pd = 1, 6, 7, 64, 20, 3, 3, (1, 2), (1, 1)
+    x = np.full((N, H, W, C), -128, np.int8)
+    f = np.full((Co, Kh, Kw, C), -128, np.int8)
+    want = oracle.conv2d_s8(x, f, st, pd)
+    for v in range(lb.LB_NUM_VARIANTS):
+        np.testing.assert_array_equal(run_conv("s8", x, f, st, pd, v), want)
