@@ -14,7 +14,9 @@ oracle timed on a bounded sample of the same workload.  Extra fields report the
 int4 and int8 GEMMs at 4096^3, the 1-bit GEMM at 4096 x 4096 x 8192 bits and the
 int8 linear layer, each with its selected and default variants (kernel time from
 HIP-graph replays, so that host launch cost is excluded), and, as context, the
-vendor library's int8 GEMM (hipBLASLt via torch._int_mm) at the same sizes.
+vendor library's int8 GEMM (hipBLASLt via torch._int_mm) at the same sizes; and
+four low-bit convolution layers with their roofline and the time of the dense
+GEMM of the same M, N, K.  ``--workload`` also accepts a convolution layer.
 
 Usage: python bench.py [--gpus 1] [--steps 300] [--warmup 100]
 """
@@ -42,6 +44,15 @@ WORKLOADS = {
     "b1_gemm_4096x4096x8192": ("b1", 4096, 4096, 8192, (3001, 3002)),
     "s8_linear_8192x11008x4096": ("linear", 8192, 11008, 4096, (5001, 5002, 5003, 5004)),
     "s8_gemm_256": ("s8", 256, 256, 256, (1001, 1002)),
+}
+
+# Convolution layers (synthetic NHWC batches; shapes of common CNN stages, not
+# a published benchmark suite): name -> (dtype, N, H, W, C, Co, Kh, Kw, stride, pad, seeds)
+CONV_LAYERS = {
+    "s8_conv3x3_n32_56x56x64": ("s8", 32, 56, 56, 64, 64, 3, 3, (1, 1), (1, 1), (6001, 6002)),
+    "s8_conv3x3_n128_14x14x256": ("s8", 128, 14, 14, 256, 256, 3, 3, (1, 1), (1, 1), (6003, 6004)),
+    "s4_conv3x3_n128_14x14x256": ("s4", 128, 14, 14, 256, 256, 3, 3, (1, 1), (1, 1), (6005, 6006)),
+    "s8_conv1x1_n128_14x14x1024": ("s8", 128, 14, 14, 1024, 256, 1, 1, (1, 1), (0, 0), (6007, 6008)),
 }
 
 
@@ -99,6 +110,60 @@ def step_fn(dtype, ops_, out, lb):
         return lb.lb_select_variant(code, M, N, K, 0)[0]
     run.selected = selected
     return run, (M, N, K)
+
+
+def conv_step(name, torch, lb):
+    """One convolution call with automatic variant choice; returns run, (M, N, K), bytes."""
+    import inputs
+    dtype, N, H, W, C, Co, Kh, Kw, st, pd, seeds = CONV_LAYERS[name]
+    mk = inputs.s8_nhwc if dtype == "s8" else inputs.s4_nhwc
+    X = torch.from_numpy(mk(N, H, W, C, seeds[0])).cuda()
+    F = torch.from_numpy(mk(Co, Kh, Kw, C, seeds[1])).cuda()
+    Ho, Wo = lb.conv_out_dims(H, W, Kh, Kw, st, pd)
+    Y = torch.empty((N, Ho, Wo, Co), dtype=torch.int32, device="cuda")
+    fn = lb.lb_conv2d_s8 if dtype == "s8" else lb.lb_conv2d_s4
+    M, K = N * Ho * Wo, Kh * Kw * C
+
+    def run(variant=None):
+        v = lb.LB_AUTO if variant is None else variant
+        fn(X, F, Y, st, pd, v)
+        return v
+
+    def selected():
+        return lb.lb_select_variant(lb.LB_S8 if dtype == "s8" else lb.LB_S4, M, Co, K, 0)[0]
+    run.selected = selected
+    nbytes = X.numel() + F.numel() + 4 * Y.numel()
+    return run, (M, Co, K), nbytes
+
+
+def conv_roofline(ops, nbytes, t):
+    """Bound of a convolution from its algorithmic intensity against the MFMA ridge."""
+    if ops / nbytes >= PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        a = ops / t / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": round(PEAK_INT8_TOPS, 1),
+                "unit": "TOP/s", "frac": round(a / PEAK_INT8_TOPS, 4)}
+    a = nbytes / t / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4)}
+
+
+def measure_conv(name, torch, lb):
+    """Convolution layer: kernel time (HIP-graph replay), its roofline, and the
+    GEMM of the same M, N, K on dense operands (the cost of gathering windows)."""
+    from bit_integer_gemm_amd.sweep import time_calls
+    dtype = CONV_LAYERS[name][0]
+    run, (M, N, K), nbytes = conv_step(name, torch, lb)
+    sel = run.selected()
+    t, _ = time_calls(lambda: run(sel), torch, target_ms=30.0, groups=5)
+    ops_ = make_operands(dtype, M, N, K, (7001, 7002), torch)
+    out = out_buffer(dtype, M, N, torch)
+    grun, _ = step_fn(dtype, ops_, out, lb)
+    tg, _ = time_calls(lambda: grun(sel), torch, target_ms=30.0, groups=5)
+    ops = 2.0 * M * N * K
+    return {"gemm_shape": [M, N, K], "variant": sel, "us_per_call": round(t * 1e6, 2),
+            "tops": round(ops / t / 1e12, 2), "roofline": conv_roofline(ops, nbytes, t),
+            "algorithmic_bytes": nbytes, "same_shape_gemm_us": round(tg * 1e6, 2),
+            "conv_over_gemm_time": round(t / tg, 4)}
 
 
 def time_steps(run, steps, warmup, torch, variant=None):
@@ -201,7 +266,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--prewarm-ms", type=float, default=150.0,
                     help="untimed steps before the warmup steps, to let the GPU reach steady clocks")
-    ap.add_argument("--workload", default="s4_gemm_4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="s4_gemm_4096", choices=sorted(WORKLOADS) + sorted(CONV_LAYERS))
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of A in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
@@ -232,10 +297,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     props = torch.cuda.get_device_properties(0)
 
-    dtype, M, N, K, seeds = WORKLOADS[args.workload]
-    ops_ = make_operands(dtype, M, N, K, seeds, torch)
-    out = out_buffer(dtype, M, N, torch)
-    run, (M, N, K) = step_fn(dtype, ops_, out, lb)
+    conv = args.workload in CONV_LAYERS
+    if conv:
+        dtype, seeds = CONV_LAYERS[args.workload][0], CONV_LAYERS[args.workload][-1]
+        run, (M, N, K), conv_bytes = conv_step(args.workload, torch, lb)
+    else:
+        dtype, M, N, K, seeds = WORKLOADS[args.workload]
+        ops_ = make_operands(dtype, M, N, K, seeds, torch)
+        out = out_buffer(dtype, M, N, torch)
+        run, (M, N, K) = step_fn(dtype, ops_, out, lb)
     variant = run.selected()
     run()
     torch.cuda.synchronize()
@@ -281,6 +351,15 @@ def main():
         "kernel_src_sha": sha,
         "timed_wall_s": round(wall, 4),
     }
+    if conv:
+        geom = CONV_LAYERS[args.workload]
+        result["metric"] = "low-bit convolution TOPS (NHWC, windows gathered into the GEMM)"
+        result["config"].update({"conv": {"N": geom[1], "H": geom[2], "W": geom[3], "C": geom[4],
+                                          "Co": geom[5], "Kh": geom[6], "Kw": geom[7],
+                                          "stride": list(geom[8]), "pad": list(geom[9])}})
+        rl = conv_roofline(ops, conv_bytes, t / args.steps)
+        rl["traffic"] = traffic
+        result["roofline"] = rl
     if traffic is None:
         result["roofline"]["traffic_note"] = traffic_note
 
@@ -288,9 +367,11 @@ def main():
         extras = {}
         for w in ("s4_gemm_4096", "s8_gemm_4096", "b1_gemm_4096x4096x8192", "s8_linear_8192x11008x4096"):
             extras[w] = measure(w, torch, lb)
+        for w in CONV_LAYERS:
+            extras[w] = measure_conv(w, torch, lb)
         result["extras"] = extras
 
-    if not args.only and not args.no_cpu_baseline:
+    if not args.only and not args.no_cpu_baseline and not conv:
         result["cpu_baseline"] = cpu_baseline(dtype if dtype != "linear" else "s8", M, N, K, seeds,
                                               min(args.cpu_rows, M))
         cb = result["cpu_baseline"]["value"]
