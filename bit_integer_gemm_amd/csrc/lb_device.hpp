@@ -54,6 +54,16 @@ __device__ inline void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_base)
                  : "v"(voff), "s"(rsrc), "s"(lds_base)
                  : "memory", "m0");
 }
+// The same with 4 bytes per lane: lane i's word lands at LDS byte lds_base + 4*i.
+__device__ inline void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Wait until at most N of this wave's copies are outstanding and its LDS reads

@@ -119,7 +119,12 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     const float *__restrict__ sx, const float *__restrict__ sw,
     int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n, ConvGeom g)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE_BYTES];
+    // Linear layer: the tile's row and column scales follow the stage ring
+    // (medium and large tiles; the small tile keeps its five workgroups per CU
+    // and reads the scales from global memory).
+    constexpr bool LDS_SCALES = KIND == KIND_LINEAR && C::BM >= 128;
+    constexpr int SCALE_BYTES = LDS_SCALES ? (C::BM + C::BN) * 4 : 0;
+    __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE_BYTES + SCALE_BYTES];
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -225,6 +230,22 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     const int64_t nk = ((int64_t)Kb + C::BK - 1) / C::BK;
     const bool k_tail = (Kb % C::BK) != 0;
 
+    // Linear layer: wave 0 copies sx[m0 .. m0+BM) and sw[n0 .. n0+BN) into LDS
+    // ahead of the first stage (entries past M or N read as zero).  These copies
+    // are older than every stage copy, so the first stage wait covers them, and
+    // the epilogue reads the scales from LDS instead of waiting on global loads
+    // at the end of the tile (5% of the layer's time at 8192 x 11008 x 4096).
+    if constexpr (LDS_SCALES) {
+        if (wave == 0) {
+            const uint32_t sbase = smem_base + C::ST * C::STAGE_BYTES;
+            const i32x4 rx = make_rsrc(sx + m0, (uint64_t)(M - m0) * 4);
+            const i32x4 rw = make_rsrc(sw + n0, (uint64_t)(N - n0) * 4);
+#pragma unroll
+            for (int q = 0; q < C::BM / 64; ++q) dma4(rx, lane * 4 + q * 256, sbase + q * 256);
+#pragma unroll
+            for (int q = 0; q < C::BN / 64; ++q) dma4(rw, lane * 4 + q * 256, sbase + C::BM * 4 + q * 256);
+        }
+    }
 #pragma unroll
     for (int s = 0; s < C::ST - 1; ++s)
         if (s < nk) issue(s, s);
@@ -278,12 +299,14 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
 
     // Epilogue: lane holds C[m][n..n+3] for each fragment.
     const bool vec_ok = (N & 3) == 0;
+    const float *lds_sx = (const float *)(smem + C::ST * C::STAGE_BYTES);
+    const float *lds_sw = lds_sx + C::BM;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
         const int64_t m = m0 + wm * C::TM + i * 16 + (lane % 16);
         if (m >= M) continue;
         float scale_m = 0.f;
-        if constexpr (KIND == KIND_LINEAR) scale_m = sx[m];
+        if constexpr (KIND == KIND_LINEAR) scale_m = LDS_SCALES ? lds_sx[m - m0] : sx[m];
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
             const int64_t n = n0 + wn * C::TN + j * 16 + (lane / 16) * 4;
@@ -293,7 +316,8 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
             if constexpr (KIND == KIND_LINEAR) {
                 float *o = (float *)out + m * (int64_t)N + n;
                 if (vec_ok) {
-                    const f32x4 s = *(const f32x4 *)(sw + n);
+                    const f32x4 s = LDS_SCALES ? *(const f32x4 *)(lds_sw + (n - n0))
+                                               : *(const f32x4 *)(sw + n);
                     f32x4 r;
                     r.x = ((float)v.x * scale_m) * s.x;
                     r.y = ((float)v.y * scale_m) * s.y;
@@ -301,7 +325,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                     r.w = ((float)v.w * scale_m) * s.w;
                     *(f32x4 *)o = r;
                 } else {
-                    for (int r = 0; r < 4 && n + r < N; ++r) o[r] = ((float)v[r] * scale_m) * sw[n + r];
+                    for (int r = 0; r < 4 && n + r < N; ++r) o[r] = ((float)v[r] * scale_m) * (LDS_SCALES ? lds_sw[n - n0 + r] : sw[n + r]);
                 }
             } else {
                 int32_t *o = (int32_t *)out + m * (int64_t)N + n;
