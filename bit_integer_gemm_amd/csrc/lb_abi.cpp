@@ -61,7 +61,8 @@ int lb_gemm_b1(const uint32_t *A, const uint32_t *B, int32_t *C, int64_t M, int6
     int st = check_common(A, B, C, M, N, K, LB_B1_K_ALIGN, LB_B1_K_MAX, variant);
     if (st != LB_OK) return st;
     const int v = resolve(LB_B1, variant, M, N, K);
-    return finish(lb::launch_b1(v, A, B, C, M, N, K / 32, (hipStream_t)stream));
+    return finish(lb::launch_mfma(lb::KIND_B1, v, A, B, C, nullptr, nullptr, M, N, K / 8,
+                                  (hipStream_t)stream));
 }
 
 int lb_gemm_s8_linear(const int8_t *X, const int8_t *W, const float *sx, const float *sw,
@@ -166,16 +167,16 @@ int lb_variant_info(int dtype, int variant, int *tile_m, int *tile_n, int *tile_
     int bk = 0;
     switch (dtype) {
     case LB_S8:
-        if (lb::mfma_variant_info(variant, tile_m, tile_n, &bk, stages)) return LB_ERR_VARIANT;
+        if (lb::mfma_variant_info(lb::KIND_S8, variant, tile_m, tile_n, &bk, stages)) return LB_ERR_VARIANT;
         *tile_k = bk;
         return LB_OK;
     case LB_S4:
-        if (lb::mfma_variant_info(variant, tile_m, tile_n, &bk, stages)) return LB_ERR_VARIANT;
+        if (lb::mfma_variant_info(lb::KIND_S4, variant, tile_m, tile_n, &bk, stages)) return LB_ERR_VARIANT;
         *tile_k = 2 * bk;
         return LB_OK;
     case LB_B1:
-        if (lb::b1_variant_info(variant, tile_m, tile_n, &bk, stages)) return LB_ERR_VARIANT;
-        *tile_k = 32 * bk;
+        if (lb::mfma_variant_info(lb::KIND_B1, variant, tile_m, tile_n, &bk, stages)) return LB_ERR_VARIANT;
+        *tile_k = 8 * bk;
         return LB_OK;
     default: return LB_ERR_VARIANT;
     }

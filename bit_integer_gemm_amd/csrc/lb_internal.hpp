@@ -6,14 +6,16 @@
 
 namespace lb {
 
-enum { KIND_S8 = 0, KIND_S4 = 1, KIND_LINEAR = 2 };
+enum { KIND_S8 = 0, KIND_S4 = 1, KIND_LINEAR = 2, KIND_B1 = 3 };
 
-// int8 MFMA family (int8 GEMM, packed-int4 GEMM, int8 linear layer).
-// Kb is the row length of A and B in bytes (K for int8, K/2 for int4).
+// int8 MFMA family (int8 GEMM, packed-int4 GEMM, int8 linear layer, and the
+// 1-bit GEMM whose bits are expanded to int8 bytes in registers).  Kb is the
+// row length of A and B in bytes (K for int8, K/2 for int4, K/8 for 1-bit).
 hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void *out,
                        const float *sx, const float *sw, int64_t M, int64_t N, int64_t Kb,
                        hipStream_t s);
-int mfma_variant_info(int variant, int *bm, int *bn, int *bk_bytes, int *stages);
+// Workgroup tile and stage of a variant; bk_bytes is the K depth of a stage in bytes.
+int mfma_variant_info(int kind, int variant, int *bm, int *bn, int *bk_bytes, int *stages);
 
 // Geometry of a convolution run as a GEMM whose A rows are gathered from an
 // NHWC image: output pixel r = (n*Ho + ho)*Wo + wo is row r, the filter taps
@@ -26,11 +28,6 @@ struct ConvGeom {
 // kind KIND_S8 or KIND_S4; M = N*Ho*Wo, N = Co, Kb = Kh*Kw*Cb.
 hipError_t launch_conv(int kind, int variant, const void *X, const void *F, int32_t *Y,
                        int64_t M, int64_t N, int64_t Kb, const ConvGeom &g, hipStream_t s);
-
-// 1-bit VALU family.  Kw is the row length in 32-bit words (K/32).
-hipError_t launch_b1(int variant, const uint32_t *A, const uint32_t *B, int32_t *C, int64_t M,
-                     int64_t N, int64_t Kw, hipStream_t s);
-int b1_variant_info(int variant, int *bm, int *bn, int *bk_words, int *stages);
 
 // Measured selection table lookup (host only).
 int select_from_table(int dtype, int64_t M, int64_t N, int64_t K, int cu_count, int *best,

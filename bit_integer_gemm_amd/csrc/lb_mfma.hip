@@ -1,4 +1,5 @@
-// lb_mfma.hip -- int8 / int4 GEMM and the int8 linear layer on gfx950 int8 MFMA.
+// lb_mfma.hip -- int8 / int4 / 1-bit GEMM, the int8 linear layer and the
+// low-bit convolution on gfx950 int8 MFMA.
 //
 // What is computed: C = A x B with exact int32 accumulation for 8-bit and
 // 4-bit operands (digest of "Leveraging Large-Scale Data for Efficient Low-Bit
@@ -35,6 +36,16 @@
 //    k): every nibble moves to the top of its own byte, i.e. the int8 value
 //    16*v with v's sign bit as the byte's sign bit.  MFMA then sums 256*a*b
 //    exactly and an arithmetic shift by 8 recovers C.
+//  * 1-bit: the LDS holds packed bits, 64 bytes = 512 values of K per block
+//    row, and a fragment read gives each lane 128 bits of its row.  Every
+//    16 of them are expanded in registers to 16 bytes of 0/1 (four bits at a
+//    time: x = 4-bit field, (x * 0x00204081) & 0x01010101 puts bit b in byte
+//    b), and the int8 MFMA sums the products exactly, eight MFMA steps per
+//    64-byte block.  The AND of two bits is their product, so this is the
+//    same popcount(a AND b) sum, at the matrix cores' rate instead of the
+//    vector ALUs'.  A lane's 16-bit piece for step s covers bits
+//    128*(lane/16) + 16*s .. +15 of the block for A and B alike, which is a
+//    permutation of K shared by both operands.
 //  * Rows past M or N read as zero through the buffer range check; a partial
 //    last K stage has its out-of-range A pieces zeroed in LDS before use.
 //  * Convolution (the im2win convolution summary, gist.science paper
@@ -111,6 +122,20 @@ __device__ inline void wait_outstanding(int tiles_after)
 __device__ inline i32x4 mfma16(i32x4 a, i32x4 b, i32x4 c)
 {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Bits off .. off+15 of w as 16 bytes of 0 or 1 (bit off+b -> byte b).  For a
+// 4-bit field x the partial products x, x<<7, x<<14, x<<21 do not overlap, so
+// bit b of x lands alone at bit 8b and the mask keeps exactly those bits.
+__device__ inline i32x4 bits_to_bytes(uint32_t w, uint32_t off)
+{
+    i32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t x = __builtin_amdgcn_ubfe(w, off + 4 * q, 4);
+        r[q] = (int)((x * 0x00204081u) & 0x01010101u);
+    }
+    return r;
 }
 
 template <class C, int KIND, bool CONV>
@@ -288,6 +313,20 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                         acc[i][j] = mfma16(bhi, ahi[i], acc[i][j]);
                     }
                 }
+            } else if constexpr (KIND == KIND_B1) {
+#pragma unroll
+                for (int st = 0; st < 8; ++st) {
+                    i32x4 ea[C::FM];
+#pragma unroll
+                    for (int i = 0; i < C::FM; ++i)
+                        ea[i] = bits_to_bytes((uint32_t)af[i][st / 2], (st % 2) * 16);
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j) {
+                        const i32x4 eb = bits_to_bytes((uint32_t)bf[j][st / 2], (st % 2) * 16);
+#pragma unroll
+                        for (int i = 0; i < C::FM; ++i) acc[i][j] = mfma16(eb, ea[i], acc[i][j]);
+                    }
+                }
             } else {
 #pragma unroll
                 for (int i = 0; i < C::FM; ++i)
@@ -355,6 +394,14 @@ using M4 = MfmaCfg<128, 128, 64, 2, 2, 4>;    // 64 KiB
 using L2 = MfmaCfg<256, 256, 128, 4, 4, 2>;   // 128 KiB, 16 waves of 64x64
 using L3 = MfmaCfg<256, 256, 64, 4, 4, 3>;    // 96 KiB
 using L4 = MfmaCfg<256, 256, 64, 4, 4, 4>;    // 128 KiB
+// 1-bit large tile: 8 waves of 64 x 128.  The in-register bit expansion costs
+// VALU work per fragment, and a wider wave tile needs fewer fragments per
+// MFMA (12 per 32 instead of 8 per 16); LDS traffic is an eighth of int8's, so
+// fewer waves lose nothing there.  Measured at 4096 x 4096 x 8192 bits: 124 us
+// against 137 us for the 16-wave int8 layout.
+using B1L2 = MfmaCfg<256, 256, 128, 4, 2, 2>; // 128 KiB
+using B1L3 = MfmaCfg<256, 256, 64, 4, 2, 3>;  // 96 KiB
+using B1L4 = MfmaCfg<256, 256, 64, 4, 2, 4>;  // 128 KiB
 
 template <class C, int KIND, bool CONV>
 static hipError_t launch_one(const void *A, const void *B, void *out, const float *sx,
@@ -388,10 +435,22 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     case 3: return launch_one<M2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
     case 4: return launch_one<M3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
     case 5: return launch_one<M4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    case 6: return launch_one<L2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    case 7: return launch_one<L3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    case 8: return launch_one<L4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    default: return hipErrorInvalidValue;
+    default: break;
+    }
+    if constexpr (KIND == KIND_B1) {
+        switch (variant) {
+        case 6: return launch_one<B1L2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+        case 7: return launch_one<B1L3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+        case 8: return launch_one<B1L4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (variant) {
+        case 6: return launch_one<L2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+        case 7: return launch_one<L3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+        case 8: return launch_one<L4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+        default: return hipErrorInvalidValue;
+        }
     }
 }
 
@@ -405,6 +464,7 @@ hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void
     case KIND_S4: return dispatch<KIND_S4, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
     case KIND_LINEAR:
         return dispatch<KIND_LINEAR, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
+    case KIND_B1: return dispatch<KIND_B1, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -419,8 +479,16 @@ hipError_t launch_conv(int kind, int variant, const void *X, const void *F, int3
     }
 }
 
-int mfma_variant_info(int variant, int *bm, int *bn, int *bk_bytes, int *stages)
+int mfma_variant_info(int kind, int variant, int *bm, int *bn, int *bk_bytes, int *stages)
 {
+    if (kind == KIND_B1) {
+        switch (variant) {
+        case 6: info_one<B1L2>(bm, bn, bk_bytes, stages); return 0;
+        case 7: info_one<B1L3>(bm, bn, bk_bytes, stages); return 0;
+        case 8: info_one<B1L4>(bm, bn, bk_bytes, stages); return 0;
+        default: break;
+        }
+    }
     switch (variant) {
     case 0: info_one<S2>(bm, bn, bk_bytes, stages); return 0;
     case 1: info_one<S3>(bm, bn, bk_bytes, stages); return 0;
