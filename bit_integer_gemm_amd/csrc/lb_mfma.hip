@@ -37,15 +37,14 @@
 //    16*v with v's sign bit as the byte's sign bit.  MFMA then sums 256*a*b
 //    exactly and an arithmetic shift by 8 recovers C.
 //  * 1-bit: the LDS holds packed bits, 64 bytes = 512 values of K per block
-//    row, and a fragment read gives each lane 128 bits of its row.  Every
-//    16 of them are expanded in registers to 16 bytes of 0/1 (four bits at a
-//    time: x = 4-bit field, (x * 0x00204081) & 0x01010101 puts bit b in byte
-//    b), and the int8 MFMA sums the products exactly, eight MFMA steps per
-//    64-byte block.  The AND of two bits is their product, so this is the
-//    same popcount(a AND b) sum, at the matrix cores' rate instead of the
-//    vector ALUs'.  A lane's 16-bit piece for step s covers bits
-//    128*(lane/16) + 16*s .. +15 of the block for A and B alike, which is a
-//    permutation of K shared by both operands.
+//    row, and a fragment read gives each lane 16 bytes (128 bits) of its row.
+//    MFMA step s (0..7) takes bit s of each of those 16 bytes: (w >> s) &
+//    0x01010101 per dword turns them into 16 bytes of 0/1, and the int8 MFMA
+//    sums the products exactly, eight steps per 64-byte block.  The AND of two
+//    bits is their product, so this is the same popcount(a AND b) sum, at the
+//    matrix cores' rate instead of the vector ALUs'.  Byte j of step s is K
+//    index 128*(lane/16) + 8*j + s of the block for A and B alike, a
+//    permutation of K that both operands share.
 //  * Rows past M or N read as zero through the buffer range check; a partial
 //    last K stage has its out-of-range A pieces zeroed in LDS before use.
 //  * Convolution (the im2win convolution summary, gist.science paper
@@ -57,6 +56,8 @@
 //    bytes per pixel are a multiple of 64, so one 64-byte K block sits inside
 //    a single tap; pieces that fall in the zero padding (or past M or K) get
 //    an offset with bit 31 set, beyond the buffer range, and load zero.
+#include <type_traits>
+
 #include "lb_device.hpp"
 #include "lb_internal.hpp"
 
@@ -124,18 +125,13 @@ __device__ inline i32x4 mfma16(i32x4 a, i32x4 b, i32x4 c)
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Bits off .. off+15 of w as 16 bytes of 0 or 1 (bit off+b -> byte b).  For a
-// 4-bit field x the partial products x, x<<7, x<<14, x<<21 do not overlap, so
-// bit b of x lands alone at bit 8b and the mask keeps exactly those bits.
-__device__ inline i32x4 bits_to_bytes(uint32_t w, uint32_t off)
+// Bit s of each byte of a 16-byte fragment piece, as a byte of 0 or 1.
+template <int S>
+__device__ inline i32x4 bit_plane(i32x4 w)
 {
-    i32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t x = __builtin_amdgcn_ubfe(w, off + 4 * q, 4);
-        r[q] = (int)((x * 0x00204081u) & 0x01010101u);
-    }
-    return r;
+    const u32x4 u = (u32x4)w;
+    if constexpr (S == 0) return (i32x4)(u & 0x01010101u);
+    else return (i32x4)((u >> S) & 0x01010101u);
 }
 
 template <class C, int KIND, bool CONV>
@@ -314,19 +310,26 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                     }
                 }
             } else if constexpr (KIND == KIND_B1) {
-#pragma unroll
-                for (int st = 0; st < 8; ++st) {
+                auto step = [&](auto sc) {
+                    constexpr int st = decltype(sc)::value;
                     i32x4 ea[C::FM];
 #pragma unroll
-                    for (int i = 0; i < C::FM; ++i)
-                        ea[i] = bits_to_bytes((uint32_t)af[i][st / 2], (st % 2) * 16);
+                    for (int i = 0; i < C::FM; ++i) ea[i] = bit_plane<st>(af[i]);
 #pragma unroll
                     for (int j = 0; j < C::FN; ++j) {
-                        const i32x4 eb = bits_to_bytes((uint32_t)bf[j][st / 2], (st % 2) * 16);
+                        const i32x4 eb = bit_plane<st>(bf[j]);
 #pragma unroll
                         for (int i = 0; i < C::FM; ++i) acc[i][j] = mfma16(eb, ea[i], acc[i][j]);
                     }
-                }
+                };
+                step(std::integral_constant<int, 0>{});
+                step(std::integral_constant<int, 1>{});
+                step(std::integral_constant<int, 2>{});
+                step(std::integral_constant<int, 3>{});
+                step(std::integral_constant<int, 4>{});
+                step(std::integral_constant<int, 5>{});
+                step(std::integral_constant<int, 6>{});
+                step(std::integral_constant<int, 7>{});
             } else {
 #pragma unroll
                 for (int i = 0; i < C::FM; ++i)
