@@ -57,13 +57,17 @@ CONV_LAYERS = {
 }
 
 
+# Sources that define the device code of the GEMM kernels (not the host-side
+# selection table or ABI checks): counter profiles stay valid while these match.
+KERNEL_SOURCES = ("lb_device.hpp", "lb_internal.hpp", "lb_mfma.hip")
+
+
 def kernel_source_sha() -> str:
     d = os.path.join(ROOT, "bit_integer_gemm_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp", ".cpp", ".inc")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in KERNEL_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
