@@ -129,6 +129,22 @@ def test_extreme_values_at_max_k():
         assert (run("b1", fives, aas, v) == 0).all()
 
 
+def test_b1_equals_int8_gemm_of_unpacked_bits():
+    """The 1-bit route against the int8 route on the GPU: unpacking the bits to
+    0/1 bytes and running the int8 GEMM must give the same C, for K values that
+    end inside a 16-byte piece, a 64-byte block and a pipeline stage."""
+    g = inputs.rng(91)
+    for (M, N, K) in [(37, 53, 128), (70, 90, 640), (300, 130, 4224), (256, 256, 8192)]:
+        Ab = g.integers(0, 2, (M, K), dtype=np.uint8)
+        Bb = g.integers(0, 2, (N, K), dtype=np.uint8)
+        A1, B1 = inputs.pack_b1(Ab), inputs.pack_b1(Bb)
+        C8 = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        lb.lb_gemm_s8(to_dev(Ab.astype(np.int8)), to_dev(Bb.astype(np.int8)), C8)
+        torch.cuda.synchronize()
+        for v in [lb.LB_AUTO] + list(range(lb.LB_NUM_VARIANTS)):
+            np.testing.assert_array_equal(run("b1", A1, B1, v), C8.cpu().numpy(), err_msg=f"{M}x{N}x{K} v{v}")
+
+
 def test_transpose_identity_on_gpu():
     M, N, K = 200, 333, 528
     A, B = make("s8", M, N, K, 77)
