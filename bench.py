@@ -277,6 +277,10 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--only", action="store_true",
                     help="time only the workload (for profiler runs): no extras, no CPU leg")
+    ap.add_argument("--variant", type=int, default=None,
+                    help="force one kernel variant (0..8) instead of the library's choice (A/B profiling)")
+    ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"), default=None,
+                    help="override M, N, K of a GEMM workload (A/B profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (the reference for HBM byte counters) and exit")
     args = ap.parse_args()
@@ -303,15 +307,24 @@ def main():
     props = torch.cuda.get_device_properties(0)
 
     conv = args.workload in CONV_LAYERS
+    if conv and args.shape:
+        sys.exit("--shape applies to GEMM workloads only")
     if conv:
         dtype, seeds = CONV_LAYERS[args.workload][0], CONV_LAYERS[args.workload][-1]
         run, (M, N, K), conv_bytes = conv_step(args.workload, torch, lb)
     else:
         dtype, M, N, K, seeds = WORKLOADS[args.workload]
+        if args.shape:
+            M, N, K = args.shape
         ops_ = make_operands(dtype, M, N, K, seeds, torch)
         out = out_buffer(dtype, M, N, torch)
         run, (M, N, K) = step_fn(dtype, ops_, out, lb)
-    variant = run.selected()
+    variant = run.selected() if args.variant is None else args.variant
+    if args.variant is not None:
+        auto_run = run
+
+        def run(v=None):
+            return auto_run(args.variant if v is None else v)
     run()
     torch.cuda.synchronize()
     # The GPU raises its clocks over the first ~30 ms of sustained work; run
@@ -346,6 +359,7 @@ def main():
                   "linear": "int8 (int32 acc) + fp32 dequant"}[dtype],
         "data": "synthetic (seeded uniform operands, resident in HBM)",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "variant": variant,
+                   "variant_forced": args.variant is not None,
                    "variant_tile": lb.lb_variant_info({"s8": 0, "s4": 1, "b1": 2, "linear": 0}[dtype], variant),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(value, 2),
