@@ -10,8 +10,10 @@ Outputs are written into buffers with guard bands on both sides that must come
 back untouched.  Small shapes cover ragged M, N (not multiples of any tile), K
 shorter than one pipeline stage, K not a multiple of the stage, and single rows
 and columns.  The full-size workloads run in the launch configuration the
-benchmark times (automatic variant choice) and are checked on sampled full rows
-and columns against the oracle plus a Freivalds product check over all of C.
+benchmark times (automatic variant choice) and are checked element by element
+against the oracle, plus a Freivalds product check; the variant sweep's shape
+grid runs with the selected variant, compared in full or (large shapes) on
+sampled rows and columns.
 """
 import numpy as np
 import pytest
@@ -185,11 +187,14 @@ def freivalds(kind, A, B, C, rng, reps=2):
 
 
 @pytest.mark.parametrize("kind,M,N,K,seeds", [
+    ("s8", 256, 256, 256, inputs.SEEDS["s8_256"]),
     ("s4", 4096, 4096, 4096, inputs.SEEDS["s4_4096"]),
     ("b1", 4096, 4096, 8192, inputs.SEEDS["b1_4096"]),
     ("s8", 4096, 4096, 4096, (4_000_001, 4_500_001)),
 ])
-def test_full_size_sampled(kind, M, N, K, seeds):
+def test_full_size_exact(kind, M, N, K, seeds):
+    """The benchmark workloads at their full sizes, automatic variant: every
+    element of C against the oracle, plus a Freivalds product check."""
     print(f"[parity] full {kind} {M}x{N}x{K}", flush=True)
     if kind == "s8":
         A, B = inputs.s8_rows(M, K, seeds[0]), inputs.s8_rows(N, K, seeds[1])
@@ -198,9 +203,46 @@ def test_full_size_sampled(kind, M, N, K, seeds):
     else:
         A, B = inputs.b1_rows(M, K, seeds[0]), inputs.b1_rows(N, K, seeds[1])
     C = run(kind, A, B, lb.LB_AUTO, K)
-    g = inputs.rng(12345)
-    sampled_check(kind, A, B, K, C, g)
-    freivalds(kind, A, B, C, g)
+    np.testing.assert_array_equal(C, ref(kind, A, B, K))
+    freivalds(kind, A, B, C, inputs.rng(12345))
+
+
+# The shape grid of the variant sweep (M, N over 64 .. 16384, four K per bit
+# width), on the sweep's own operands, with the variant the library selects for
+# each shape.  Shapes up to 2^22 outputs are covered (240 per bit width); the
+# larger ones run the same kernels and are covered by the full-size workloads
+# above and by the sweep's check that all nine variants agree.
+GRID_MN = [2 ** e for e in range(6, 15)]
+GRID_K = {"s8": [256, 1024, 4096, 8192], "s4": [256, 1024, 4096, 8192], "b1": [1024, 4096, 8192, 32768]}
+DTYPE_CODE = {"s8": 0, "s4": 1, "b1": 2}
+
+
+@pytest.mark.parametrize("kind", ["s8", "s4", "b1"])
+def test_sweep_grid_selected_variant(kind):
+    shapes = [(M, N) for M in GRID_MN for N in GRID_MN if M * N <= 1 << 22]
+    Mmax, Nmax = max(M for M, _ in shapes), max(N for _, N in shapes)
+    g = inputs.rng(777)
+    for kidx, K in enumerate(GRID_K[kind]):
+        sa = 4_000_000 + 100 * DTYPE_CODE[kind] + kidx
+        sb = 4_500_000 + 100 * DTYPE_CODE[kind] + kidx
+        rows = {"s8": inputs.s8_rows, "s4": inputs.s4_rows, "b1": inputs.b1_rows}[kind]
+        A, B = rows(Mmax, K, sa), rows(Nmax, K, sb)
+        dA, dB = to_dev(A), to_dev(B)
+        if kind == "b1":
+            dA, dB = dA.view(torch.int32), dB.view(torch.int32)
+        call = {"s8": lb.lb_gemm_s8, "s4": lb.lb_gemm_s4, "b1": lb.lb_gemm_b1}[kind]
+        print(f"[parity] grid {kind} K={K}: {len(shapes)} shapes", flush=True)
+        for M, N in shapes:
+            C = torch.empty(M, N, dtype=torch.int32, device="cuda")
+            call(dA[:M], dB[:N], C, lb.LB_AUTO)
+            torch.cuda.synchronize()
+            Ch = C.cpu().numpy()
+            if M * N * K <= 1 << 30:
+                np.testing.assert_array_equal(Ch, ref(kind, A[:M], B[:N], K), err_msg=f"{M}x{N}x{K}")
+            else:
+                sampled_check(kind, A[:M], B[:N], K, Ch, g, nrows=3, ncols=3)
+        del dA, dB
+        torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
@@ -230,18 +272,16 @@ def test_linear_small_every_variant(variant):
         assert_rel(run_linear(X, W, sx, sw, variant), oracle.linear_s8(X, W, sx, sw))
 
 
-def test_linear_full_size_sampled():
+def test_linear_full_size_exact():
+    """The linear layer 8192 x 11008 x 4096, automatic variant: every output
+    against the oracle within the relative bound."""
     M, K, N = 8192, 4096, 11008
     s = inputs.SEEDS["linear"]
     print("[parity] linear full 8192x11008x4096", flush=True)
     X, W = inputs.s8_rows(M, K, s[0]), inputs.s8_rows(N, K, s[1])
     sx, sw = inputs.scales(M, s[2]), inputs.scales(N, s[3])
     out = run_linear(X, W, sx, sw, lb.LB_AUTO)
-    g = inputs.rng(999)
-    rows = np.unique(np.concatenate([[0, M - 1], g.choice(M, 4, replace=False)]))
-    cols = np.unique(np.concatenate([[0, N - 1], g.choice(N, 4, replace=False)]))
-    assert_rel(out[rows], oracle.linear_s8(np.ascontiguousarray(X[rows]), W, sx[rows], sw))
-    assert_rel(out[:, cols], oracle.linear_s8(X, np.ascontiguousarray(W[cols]), sx, sw[cols]))
+    assert_rel(out, oracle.linear_s8(X, W, sx, sw))
 
 
 def test_graph_capture_replays_match_eager():
