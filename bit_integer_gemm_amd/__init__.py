@@ -30,7 +30,7 @@ LB_AUTO = -1
 LB_NUM_VARIANTS = 9
 LB_DEFAULT_VARIANT = 7
 K_ALIGN = {LB_S8: 16, LB_S4: 32, LB_B1: 128}
-K_MAX = {LB_S8: 131071, LB_S4: 131071, LB_B1: 134217600}
+K_MAX = {LB_S8: 131071, LB_S4: 131071, LB_B1: 33554304}
 CONV_C_ALIGN = {LB_S8: 64, LB_S4: 128}
 
 # Exported symbols of include/lb_gemm.h (checked by the CPU tests).

@@ -38,13 +38,16 @@
 //    exactly and an arithmetic shift by 8 recovers C.
 //  * 1-bit: the LDS holds packed bits, 64 bytes = 512 values of K per block
 //    row, and a fragment read gives each lane 16 bytes (128 bits) of its row.
-//    MFMA step s (0..7) takes bit s of each of those 16 bytes: (w >> s) &
-//    0x01010101 per dword turns them into 16 bytes of 0/1, and the int8 MFMA
-//    sums the products exactly, eight steps per 64-byte block.  The AND of two
-//    bits is their product, so this is the same popcount(a AND b) sum, at the
-//    matrix cores' rate instead of the vector ALUs'.  Byte j of step s is K
-//    index 128*(lane/16) + 8*j + s of the block for A and B alike, a
-//    permutation of K that both operands share.
+//    MFMA step s (0..7) takes bit s of each of those 16 bytes, and the int8
+//    MFMA sums the products exactly, eight steps per 64-byte block.  The AND
+//    of two bits is their product, so this is the same popcount(a AND b) sum,
+//    at the matrix cores' rate instead of the vector ALUs'.  Byte j of step s
+//    is K index 128*(lane/16) + 8*j + s of the block for A and B alike, a
+//    permutation of K that both operands share.  To need one AND per operand
+//    and step, A's bytes are bit-mirrored and shifted down one place once per
+//    fragment (bit s -> bit 6-s); step s < 7 keeps A's bit as 2^(6-s) and B's
+//    as 2^s, so every pair of set bits adds 64 (bit 7: 64 and 1), and the
+//    epilogue divides by 64.
 //  * Rows past M or N read as zero through the buffer range check; a partial
 //    last K stage has its out-of-range A pieces zeroed in LDS before use.
 //  * Convolution (the im2win convolution summary, gist.science paper
@@ -125,13 +128,15 @@ __device__ inline i32x4 mfma16(i32x4 a, i32x4 b, i32x4 c)
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Bit s of each byte of a 16-byte fragment piece, as a byte of 0 or 1.
-template <int S>
-__device__ inline i32x4 bit_plane(i32x4 w)
+// Bits of each byte in reverse order, then the whole word shifted down one
+// place: bit s (s < 7) of every byte lands on bit 6 - s of the same byte (bit 7
+// of each byte then holds a bit of the next byte, which no mask below keeps).
+__device__ inline i32x4 mirror_bytes_shr1(i32x4 w)
 {
-    const u32x4 u = (u32x4)w;
-    if constexpr (S == 0) return (i32x4)(u & 0x01010101u);
-    else return (i32x4)((u >> S) & 0x01010101u);
+    u32x4 u = (u32x4)w;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) u[d] = __builtin_bswap32(__builtin_bitreverse32(u[d])) >> 1;
+    return (i32x4)u;
 }
 
 template <class C, int KIND, bool CONV>
@@ -144,6 +149,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     // (medium and large tiles; the small tile keeps its five workgroups per CU
     // and reads the scales from global memory).
     constexpr bool LDS_SCALES = KIND == KIND_LINEAR && C::BM >= 128;
+    constexpr bool LATE_COPIES = C::NW == 4 || KIND == KIND_S4;
     constexpr int SCALE_BYTES = LDS_SCALES ? (C::BM + C::BN) * 4 : 0;
     __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE_BYTES + SCALE_BYTES];
 
@@ -280,7 +286,8 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
             zero_k_tail<C>(stage, lane, wave, kt * C::BK, Kb);
             barrier_lds();
         }
-        if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1, (int)((kt + C::ST - 1) % C::ST));
+        if constexpr (LATE_COPIES)
+            if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1, (int)((kt + C::ST - 1) % C::ST));
 
         const char *fstage = stage + frag_offset(lane);
 #pragma unroll
@@ -292,6 +299,19 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
                 bf[j] = *(const i32x4 *)(fstage + (C::ABLK + kb * (C::BN / 16) + wn * C::FN + j) * 1024);
+            // Large tiles: the next stage's copies go out behind this stage's
+            // first fragment reads (they fill the slot the previous iteration
+            // read, which the barrier above has released), so the LDS latency
+            // of the reads runs under the copies' address arithmetic; the MFMAs
+            // stay below them.  Measured: 1-2% faster for the large int8 and
+            // 1-bit tiles, 5% slower for the small tile.  The 16-wave int4 tile
+            // copies first: holding its fragments over the copies would spill.
+            if (kb == 0) {
+                if constexpr (!LATE_COPIES) {
+                    if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1, (int)((kt + C::ST - 1) % C::ST));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
             if constexpr (KIND == KIND_S4) {
                 i32x4 alo[C::FM], ahi[C::FM];
 #pragma unroll
@@ -310,14 +330,31 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                     }
                 }
             } else if constexpr (KIND == KIND_B1) {
+                // Bit 7 of every byte first, from the words as loaded: A's as
+                // the value 64, B's as the value 1.
+                {
+                    i32x4 ea[C::FM];
+#pragma unroll
+                    for (int i = 0; i < C::FM; ++i) ea[i] = (i32x4)(((u32x4)af[i] >> 1) & 0x40404040u);
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j) {
+                        const i32x4 eb = (i32x4)(((u32x4)bf[j] >> 7) & 0x01010101u);
+#pragma unroll
+                        for (int i = 0; i < C::FM; ++i) acc[i][j] = mfma16(eb, ea[i], acc[i][j]);
+                    }
+                }
+                // Bits 0..6: A's byte bit s moves to bit 6-s, so one AND per
+                // operand gives A's bit s as 2^(6-s) and B's as 2^s.
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i) af[i] = mirror_bytes_shr1(af[i]);
                 auto step = [&](auto sc) {
                     constexpr int st = decltype(sc)::value;
                     i32x4 ea[C::FM];
 #pragma unroll
-                    for (int i = 0; i < C::FM; ++i) ea[i] = bit_plane<st>(af[i]);
+                    for (int i = 0; i < C::FM; ++i) ea[i] = (i32x4)((u32x4)af[i] & (0x01010101u << (6 - st)));
 #pragma unroll
                     for (int j = 0; j < C::FN; ++j) {
-                        const i32x4 eb = bit_plane<st>(bf[j]);
+                        const i32x4 eb = (i32x4)((u32x4)bf[j] & (0x01010101u << st));
 #pragma unroll
                         for (int i = 0; i < C::FM; ++i) acc[i][j] = mfma16(eb, ea[i], acc[i][j]);
                     }
@@ -329,7 +366,6 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                 step(std::integral_constant<int, 4>{});
                 step(std::integral_constant<int, 5>{});
                 step(std::integral_constant<int, 6>{});
-                step(std::integral_constant<int, 7>{});
             } else {
 #pragma unroll
                 for (int i = 0; i < C::FM; ++i)
@@ -355,6 +391,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
             if (n >= N) continue;
             i32x4 v = acc[i][j];
             if constexpr (KIND == KIND_S4) v = v >> 8;
+            if constexpr (KIND == KIND_B1) v = v >> 6;
             if constexpr (KIND == KIND_LINEAR) {
                 float *o = (float *)out + m * (int64_t)N + n;
                 if (vec_ok) {

@@ -69,15 +69,15 @@ typedef enum { LB_S8 = 0, LB_S4 = 1, LB_B1 = 2 } lb_dtype;
 
 /* K limits: rows must be whole 16-byte chunks, and the worst-case |sum| must
  * fit int32 (16384 * K for int8; the int4 path accumulates 256 * a * b, the
- * same bound).  1-bit sums are at most K, so the 1-bit limit comes instead from
- * addressing: a workgroup tile spans up to 256 rows of K/8 bytes and its
- * buffer offsets are 32-bit, so K/8 * 256 must stay below 2^32 (K < 2^27). */
+ * same bound).  The 1-bit path accumulates 64 per matching bit pair (each bit
+ * position is weighted so that a pair contributes 64 whatever its place in
+ * the byte), so 64 * K must fit int32: K < 2^25. */
 #define LB_S8_K_ALIGN 16
 #define LB_S4_K_ALIGN 32
 #define LB_B1_K_ALIGN 128
 #define LB_S8_K_MAX 131071
 #define LB_S4_K_MAX 131071
-#define LB_B1_K_MAX 134217600 /* largest multiple of 128 below 2^27 */
+#define LB_B1_K_MAX 33554304 /* largest multiple of 128 below 2^25 */
 
 /*
  * C = A x B, int8 operands, int32 result.

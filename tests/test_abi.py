@@ -55,7 +55,7 @@ NULL = ctypes.c_void_p(0)
 
 
 @pytest.mark.parametrize("fn,align,kmax", [("lb_gemm_s8", 16, 131071), ("lb_gemm_s4", 32, 131071),
-                                           ("lb_gemm_b1", 128, 134217600)])
+                                           ("lb_gemm_b1", 128, 33554304)])
 def test_gemm_argument_checks(lib, fn, align, kmax):
     f = getattr(lib, fn)
     assert f(NULL, FAKE, FAKE, 4, 4, align, -1, NULL) == lb.LB_ERR_NULL

@@ -15,6 +15,8 @@ against the oracle, plus a Freivalds product check; the variant sweep's shape
 grid runs with the selected variant, compared in full or (large shapes) on
 sampled rows and columns.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -129,6 +131,29 @@ def test_extreme_values_at_max_k():
         fives = np.full((M, Kb // 32), 0x55555555, np.uint32)
         aas = np.full((N, Kb // 32), 0xAAAAAAAA, np.uint32)
         assert (run("b1", fives, aas, v) == 0).all()
+
+
+B1_MAX_K_CASE = (17, 9, lb.K_MAX[lb.LB_B1])
+
+
+@functools.lru_cache(maxsize=1)
+def b1_max_k_case():
+    M, N, K = B1_MAX_K_CASE
+    A, B = inputs.b1_rows(M, K, 31), inputs.b1_rows(N, K, 32)
+    return A, B, oracle.gemm_b1(A, B, K)
+
+
+@pytest.mark.parametrize("variant", list(range(9)))
+def test_b1_at_max_k(variant):
+    """The largest 1-bit K the boundary accepts, where the kernel's accumulator
+    (64 per matching bit pair) comes within 8192 of the int32 limit: all ones
+    give K exactly, and random bits match the oracle."""
+    M, N, K = B1_MAX_K_CASE
+    print(f"[parity] b1 K={K} v{variant}", flush=True)
+    ones = np.full((M, K // 32), 0xFFFFFFFF, np.uint32)
+    assert (run("b1", ones, ones[:N], variant) == K).all()
+    A, B, want = b1_max_k_case()
+    np.testing.assert_array_equal(run("b1", A, B, variant), want)
 
 
 def test_b1_equals_int8_gemm_of_unpacked_bits():
