@@ -14,9 +14,10 @@ simulated.
 `run` appends one JSON line per (shape, variant) and skips those already in the
 output file, so an interrupted sweep resumes.  It also checks that all nine
 variants return identical C on every shape.  `table` turns measurements into
-labels: the fastest variant, except that the default variant keeps the label
-when it is within EPS of the fastest (timing noise on short kernels must not
-make the selected variant slower than the default), and writes
+labels: the fastest variant, where every variant within EPS of the fastest
+counts as tied and a tie goes to the default variant, else to the lowest index
+(timing noise on short kernels must not make the selected variant slower than
+the default, nor flip labels between near-equal variants), and writes
 csrc/selector_table.inc.
 
 Inputs: for each K, one seeded uniform operand pair of the largest M and N is
@@ -186,9 +187,11 @@ def labels(recs, eps=EPS, default=DEFAULT):
         if any(t is None for t in ts):
             continue
         order = sorted(range(9), key=lambda v: (ts[v], v))
-        best = order[0]
-        if ts[default] <= (1 + eps) * ts[best]:
-            best = default
+        # Variants within eps of the fastest are ties: the default wins a tie,
+        # then the lowest index (fewest stages, then smallest tile), so labels
+        # do not follow timing noise between near-equal variants.
+        tied = [v for v in range(9) if ts[v] <= (1 + eps) * ts[order[0]]]
+        best = default if default in tied else min(tied)
         second = next(v for v in order if v != best)
         out[key] = (best, second, ts)
     return out
