@@ -115,3 +115,28 @@ def test_classifier_layer_math_by_hand():
     out = selector_mlp.forward_np([(W, b), (W2, np.zeros(1, np.float32))], [3.0, 1.0])
     # hidden = relu([3 - 2 + 0.25, 1.5 + 0.5 - 3]) = [1.25, 0]; out = 2 * 1.25
     assert out.tolist() == [2.5]
+
+
+def test_label_rule_ties_go_to_default_then_lowest_index():
+    """Labels from timings: variants within 2% of the fastest are tied; the
+    default wins a tie, otherwise the lowest index does; the second choice is the
+    fastest of the rest."""
+    from bit_integer_gemm_amd import sweep
+
+    def lab(times):
+        recs = {("s8", 64, 64, 256, v): {"sec": t} for v, t in enumerate(times)}
+        return sweep.labels(recs)[("s8", 64, 64, 256)][:2]
+
+    base = [10.0] * 9
+    # a clear winner
+    t = list(base); t[4] = 5.0
+    assert lab(t) == (4, 0)
+    # 8 is fastest, 6 within 2% of it: the lower index wins the tie
+    t = list(base); t[8] = 5.0; t[6] = 5.09
+    assert lab(t) == (6, 8)
+    # the default (7) within 2% wins the tie over a faster variant
+    t = list(base); t[3] = 5.0; t[7] = 5.08
+    assert lab(t) == (7, 3)
+    # just beyond 2% is not a tie
+    t = list(base); t[8] = 5.0; t[6] = 5.11
+    assert lab(t) == (8, 6)
