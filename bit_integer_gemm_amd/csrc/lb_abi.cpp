@@ -80,8 +80,8 @@ int lb_gemm_s8_linear(const int8_t *X, const int8_t *W, const float *sx, const f
 
 namespace {
 
-// Shared checks and launch of the two convolutions.  cbytes_per_c2 is 2 for
-// int8 (bytes per pixel = C) and 1 for int4 (C/2); calign is the channel rule.
+// Shared checks and launch of the two convolutions.  kind selects int8 (C bytes
+// per pixel) or int4 (C/2 bytes); calign is the channel rule, kmax the K limit.
 int conv_entry(int kind, int dtype, const void *X, const void *F, int32_t *Y, int64_t N, int64_t H,
                int64_t W, int64_t C, int64_t Co, int64_t Kh, int64_t Kw, int64_t sh, int64_t sw,
                int64_t ph, int64_t pw, int variant, void *stream, int64_t calign, int64_t kmax)
@@ -154,7 +154,8 @@ const char *lb_status_string(int status)
     case LB_ERR_SHAPE: return "non-positive or too large M, N or K";
     case LB_ERR_ALIGN: return "K violates the alignment rule for this type";
     case LB_ERR_VARIANT: return "variant or dtype out of range";
-    case LB_ERR_OVERFLOW: return "K above the limit for this type (exact int32 sum, or 1-bit addressing)";
+    case LB_ERR_OVERFLOW: return "K above the limit for this type (the exact int32 sum must fit), "
+                                 "or a convolution beyond 32-bit byte offsets";
     case LB_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
     }

@@ -57,7 +57,8 @@ typedef enum {
     LB_ERR_SHAPE = 2,    /* M, N or K is not positive */
     LB_ERR_ALIGN = 3,    /* K violates the per-type alignment rule */
     LB_ERR_VARIANT = 4,  /* variant outside LB_AUTO..8, or dtype unknown */
-    LB_ERR_OVERFLOW = 5, /* K above the type's limit (int32 sum range; 1-bit: addressing) */
+    LB_ERR_OVERFLOW = 5, /* K above the type's limit (the exact int32 sum must fit);
+                            convolutions: also 32-bit offset range */
     LB_ERR_HIP = 6       /* the HIP runtime reported an error */
 } lb_status;
 
