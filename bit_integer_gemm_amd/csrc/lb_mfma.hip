@@ -431,17 +431,21 @@ using S4 = MfmaCfg<64, 64, 128, 2, 2, 4>;     // 64 KiB
 using M2 = MfmaCfg<128, 128, 128, 2, 2, 2>;   // 64 KiB
 using M3 = MfmaCfg<128, 128, 64, 2, 2, 3>;    // 48 KiB
 using M4 = MfmaCfg<128, 128, 64, 2, 2, 4>;    // 64 KiB
-using L2 = MfmaCfg<256, 256, 128, 4, 4, 2>;   // 128 KiB, 16 waves of 64x64
-using L3 = MfmaCfg<256, 256, 64, 4, 4, 3>;    // 96 KiB
-using L4 = MfmaCfg<256, 256, 64, 4, 4, 4>;    // 128 KiB
-// 1-bit large tile: 8 waves of 64 x 128.  The in-register bit expansion costs
-// VALU work per fragment, and a wider wave tile needs fewer fragments per
-// MFMA (12 per 32 instead of 8 per 16); LDS traffic is an eighth of int8's, so
-// fewer waves lose nothing there.  Measured at 4096 x 4096 x 8192 bits: 124 us
-// against 137 us for the 16-wave int8 layout.
-using B1L2 = MfmaCfg<256, 256, 128, 4, 2, 2>; // 128 KiB
-using B1L3 = MfmaCfg<256, 256, 64, 4, 2, 3>;  // 96 KiB
-using B1L4 = MfmaCfg<256, 256, 64, 4, 2, 4>;  // 128 KiB
+// Large tile: 16 waves of 64x64 (L2W16, L4W16) or 8 waves of 64x128 (W8).
+// Fewer, wider waves need fewer fragment reads and in-register conversions per
+// MFMA (12 fragments per 32 MFMAs instead of 8 per 16) but hide less latency.
+// Measured per variant, two builds timed in one process: the 3-stage large
+// tile is 1-7% faster with 8 waves for every type, the 4-stage one 2-4% for
+// int4 and mixed for int8, and the 2-stage one mixed for int8 and int4 (the
+// 16 waves win by 4-9% when there are only 16-64 tiles).  The 1-bit kernels
+// use 8 waves throughout: their per-fragment bit work makes the wider wave
+// tile pay at every depth (124 against 137 us at 4096 x 4096 x 8192 bits with
+// the first bit expansion).
+using L2W16 = MfmaCfg<256, 256, 128, 4, 4, 2>; // 128 KiB
+using L2W8 = MfmaCfg<256, 256, 128, 4, 2, 2>;  // 128 KiB
+using L3W8 = MfmaCfg<256, 256, 64, 4, 2, 3>;   // 96 KiB
+using L4W16 = MfmaCfg<256, 256, 64, 4, 4, 4>;  // 128 KiB
+using L4W8 = MfmaCfg<256, 256, 64, 4, 2, 4>;   // 128 KiB
 
 template <class C, int KIND, bool CONV>
 static hipError_t launch_one(const void *A, const void *B, void *out, const float *sx,
@@ -477,20 +481,14 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     case 5: return launch_one<M4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
     default: break;
     }
-    if constexpr (KIND == KIND_B1) {
-        switch (variant) {
-        case 6: return launch_one<B1L2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-        case 7: return launch_one<B1L3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-        case 8: return launch_one<B1L4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-        default: return hipErrorInvalidValue;
-        }
-    } else {
-        switch (variant) {
-        case 6: return launch_one<L2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-        case 7: return launch_one<L3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-        case 8: return launch_one<L4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-        default: return hipErrorInvalidValue;
-        }
+    constexpr bool b1 = KIND == KIND_B1;
+    switch (variant) {
+    case 6: return launch_one<std::conditional_t<b1, L2W8, L2W16>, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 7: return launch_one<L3W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 8:
+        return launch_one<std::conditional_t<b1 || KIND == KIND_S4, L4W8, L4W16>, KIND, CONV>(
+            A, B, out, sx, sw, M, N, Kb, g, s);
+    default: return hipErrorInvalidValue;
     }
 }
 
@@ -521,14 +519,7 @@ hipError_t launch_conv(int kind, int variant, const void *X, const void *F, int3
 
 int mfma_variant_info(int kind, int variant, int *bm, int *bn, int *bk_bytes, int *stages)
 {
-    if (kind == KIND_B1) {
-        switch (variant) {
-        case 6: info_one<B1L2>(bm, bn, bk_bytes, stages); return 0;
-        case 7: info_one<B1L3>(bm, bn, bk_bytes, stages); return 0;
-        case 8: info_one<B1L4>(bm, bn, bk_bytes, stages); return 0;
-        default: break;
-        }
-    }
+    (void)kind;  // the large tiles' wave count varies by type, not their shape
     switch (variant) {
     case 0: info_one<S2>(bm, bn, bk_bytes, stages); return 0;
     case 1: info_one<S3>(bm, bn, bk_bytes, stages); return 0;
@@ -536,9 +527,9 @@ int mfma_variant_info(int kind, int variant, int *bm, int *bn, int *bk_bytes, in
     case 3: info_one<M2>(bm, bn, bk_bytes, stages); return 0;
     case 4: info_one<M3>(bm, bn, bk_bytes, stages); return 0;
     case 5: info_one<M4>(bm, bn, bk_bytes, stages); return 0;
-    case 6: info_one<L2>(bm, bn, bk_bytes, stages); return 0;
-    case 7: info_one<L3>(bm, bn, bk_bytes, stages); return 0;
-    case 8: info_one<L4>(bm, bn, bk_bytes, stages); return 0;
+    case 6: info_one<L2W16>(bm, bn, bk_bytes, stages); return 0;
+    case 7: info_one<L3W8>(bm, bn, bk_bytes, stages); return 0;
+    case 8: info_one<L4W16>(bm, bn, bk_bytes, stages); return 0;
     default: return -1;
     }
 }
