@@ -105,6 +105,71 @@ int device_cu_count(int *out)
     return LB_OK;
 }
 
+// Nearest measured shape of the table in log2(M, N, K) space (L1 distance).
+// The table's logarithms are taken once.
+struct TablePoint {
+    double lm, ln, lk;
+    int dtype, best, second;
+};
+
+const TablePoint *table_points()
+{
+    static const TablePoint *pts = [] {
+        TablePoint *p = new TablePoint[kTableLen > 0 ? kTableLen : 1];
+        for (int i = 0; i < kTableLen; ++i) {
+            const SelEntry &e = kTable[i];
+            p[i] = {(double)e.log2m, (double)e.log2n, std::log2((double)e.k), e.dtype, e.best, e.second};
+        }
+        return p;
+    }();
+    return pts;
+}
+
+void table_choice(int dtype, int64_t M, int64_t N, int64_t K, int *best, int *second)
+{
+    const TablePoint *pts = table_points();
+    const double lm = std::log2((double)M), ln = std::log2((double)N), lk = std::log2((double)K);
+    int bi = -1;
+    double bd = 1e300;
+    for (int i = 0; i < kTableLen; ++i) {
+        if (pts[i].dtype != dtype) continue;
+        const double d = std::fabs(lm - pts[i].lm) + std::fabs(ln - pts[i].ln) + std::fabs(lk - pts[i].lk);
+        if (d < bd) { bd = d; bi = i; }
+    }
+    if (bi < 0) {
+        *best = LB_DEFAULT_VARIANT;
+        *second = LB_DEFAULT_VARIANT + 1;
+        return;
+    }
+    *best = pts[bi].best;
+    *second = pts[bi].second;
+}
+
+void mlp_choice(int dtype, int64_t M, int64_t N, int64_t K, int cu, int *best, int *second)
+{
+    float lg[LB_NUM_VARIANTS];
+    mlp_logits(dtype, M, N, K, cu, lg);
+    int b0 = 0;
+    for (int v = 1; v < LB_NUM_VARIANTS; ++v)
+        if (lg[v] > lg[b0]) b0 = v;
+    int b1 = b0 == 0 ? 1 : 0;
+    for (int v = 0; v < LB_NUM_VARIANTS; ++v)
+        if (v != b0 && lg[v] > lg[b1]) b1 = v;
+    *best = b0;
+    *second = b1;
+}
+
+// Each thread remembers its last few answers: a library call with LB_AUTO
+// selects on every call, and repeated shapes should not pay the table scan
+// (~3 us) or the classifier (~18 us) again.  The key holds everything the
+// answer depends on, the selector mode included.
+struct CacheSlot {
+    int64_t M, N, K;
+    int dtype, cu, mode, best, second;
+    bool valid;
+};
+thread_local CacheSlot t_cache[16];
+
 }  // namespace
 
 namespace lb {
@@ -116,35 +181,19 @@ int select_from_table(int dtype, int64_t M, int64_t N, int64_t K, int cu_count, 
         int st = device_cu_count(&cu_count);
         if (st != LB_OK) return st;
     }
-    if (use_mlp(dtype)) {
-        float lg[LB_NUM_VARIANTS];
-        mlp_logits(dtype, M, N, K, cu_count, lg);
-        int b0 = 0;
-        for (int v = 1; v < LB_NUM_VARIANTS; ++v)
-            if (lg[v] > lg[b0]) b0 = v;
-        int b1 = b0 == 0 ? 1 : 0;
-        for (int v = 0; v < LB_NUM_VARIANTS; ++v)
-            if (v != b0 && lg[v] > lg[b1]) b1 = v;
-        *best = b0;
-        if (second) *second = b1;
-        return LB_OK;
+    const int mode = use_mlp(dtype) ? 1 : 0;
+    const uint64_t h = (uint64_t)M * 0x9E3779B97F4A7C15ull ^ (uint64_t)N * 0xC2B2AE3D27D4EB4Full ^
+                       (uint64_t)K * 0x165667B19E3779F9ull ^ (uint64_t)(dtype * 3 + mode) ^ (uint64_t)cu_count;
+    CacheSlot &c = t_cache[(h >> 32) & 15u];
+    if (!(c.valid && c.M == M && c.N == N && c.K == K && c.dtype == dtype && c.cu == cu_count &&
+          c.mode == mode)) {
+        int b = 0, s2 = 0;
+        if (mode) mlp_choice(dtype, M, N, K, cu_count, &b, &s2);
+        else table_choice(dtype, M, N, K, &b, &s2);
+        c = {M, N, K, dtype, cu_count, mode, b, s2, true};
     }
-    const double lm = std::log2((double)M), ln = std::log2((double)N), lk = std::log2((double)K);
-    int bi = -1;
-    double bd = 1e300;
-    for (int i = 0; i < kTableLen; ++i) {
-        const SelEntry &e = kTable[i];
-        if (e.dtype != dtype) continue;
-        const double d = std::fabs(lm - e.log2m) + std::fabs(ln - e.log2n) + std::fabs(lk - std::log2((double)e.k));
-        if (d < bd) { bd = d; bi = i; }
-    }
-    if (bi < 0) {
-        *best = LB_DEFAULT_VARIANT;
-        if (second) *second = LB_DEFAULT_VARIANT + 1;
-        return LB_OK;
-    }
-    *best = kTable[bi].best;
-    if (second) *second = kTable[bi].second;
+    *best = c.best;
+    if (second) *second = c.second;
     return LB_OK;
 }
 

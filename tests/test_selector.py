@@ -140,3 +140,33 @@ def test_label_rule_ties_go_to_default_then_lowest_index():
     # just beyond 2% is not a tie
     t = list(base); t[8] = 5.0; t[6] = 5.11
     assert lab(t) == (8, 6)
+
+
+def test_repeated_queries_and_mode_switches_agree():
+    """The library remembers recent answers per thread; a repeated query, and a
+    query after switching LB_SELECTOR back and forth, must give what a fresh
+    query in that mode gives (the mode is part of what is remembered)."""
+    shapes = [(d, 2 ** a + 3, 2 ** b + 5, 256 * (1 + k)) for d in range(3) for a, b, k in
+              ((6, 9, 0), (10, 7, 3), (13, 12, 15), (8, 14, 31))]
+    table = {s: lb.lb_select_variant(*s, 256) for s in shapes}
+    os.environ["LB_SELECTOR"] = "mlp"
+    try:
+        mlp = {s: lb.lb_select_variant(*s, 256) for s in shapes}
+        for _ in range(3):
+            for s in shapes:
+                assert lb.lb_select_variant(*s, 256) == mlp[s]
+    finally:
+        del os.environ["LB_SELECTOR"]
+    for _ in range(3):
+        for s in shapes:
+            assert lb.lb_select_variant(*s, 256) == table[s]
+    # the table answers still follow the nearest-shape rule checked above
+    ents = table_entries()
+    for (d, M, N, K), got in table.items():
+        cand = [e for e in ents if e[0] == d]
+        dist = lambda e: (abs(math.log2(M) - e[1]) + abs(math.log2(N) - e[2])  # noqa: E731
+                          + abs(math.log2(K) - math.log2(e[3])))
+        best = min(dist(e) for e in cand)
+        assert got in {(e[4], e[5]) for e in cand if abs(dist(e) - best) < 1e-12}
+    # the two modes really differ somewhere, so the test can see a stale answer
+    assert any(table[s] != mlp[s] for s in shapes)
