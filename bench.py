@@ -204,8 +204,10 @@ def load_traffic(workload: str, sha: str):
     return t.get("hbm_bytes_per_launch"), t.get("note")
 
 
-def cpu_baseline(dtype, M, N, K, seeds, rows):
-    """The CPU oracle on the first `rows` rows of A against all of B (a bounded sample)."""
+def cpu_baseline(dtype, M, N, K, seeds, rows, min_seconds=10.0, max_runs=5):
+    """The CPU oracle on the first `rows` rows of A against all of B (a bounded
+    sample), repeated until about `min_seconds` of CPU work; the rate is the
+    sample's ops over the mean time of a run."""
     import inputs
     import oracle
     if dtype == "s4":
@@ -220,13 +222,17 @@ def cpu_baseline(dtype, M, N, K, seeds, rows):
     else:
         raise ValueError(dtype)
     oracle.lib()
-    t0 = time.perf_counter()
-    f()
-    dt = time.perf_counter() - t0
+    times = []
+    while len(times) < max_runs and sum(times) < min_seconds:
+        t0 = time.perf_counter()
+        f()
+        times.append(time.perf_counter() - t0)
+    dt = sum(times) / len(times)
     return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TOPS",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{dtype} GEMM, first {rows} of {M} rows of A x all {N} columns, K={K} "
-                      f"({rows / M:.1%} of the workload), {dt:.2f} s wall"}
+                      f"({rows / M:.1%} of the workload), {len(times)} runs, "
+                      f"{dt:.2f} s wall each (mean)"}
 
 
 def measure(workload, torch, lb):
