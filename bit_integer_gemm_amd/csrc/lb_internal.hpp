@@ -9,11 +9,13 @@ namespace lb {
 enum { KIND_S8 = 0, KIND_S4 = 1, KIND_LINEAR = 2, KIND_B1 = 3 };
 
 // int8 MFMA family (int8 GEMM, packed-int4 GEMM, int8 linear layer, and the
-// 1-bit GEMM whose bits are expanded to int8 bytes in registers).  Kb is the
-// row length of A and B in bytes (K for int8, K/2 for int4, K/8 for 1-bit).
+// 1-bit GEMM on weighted bit planes).  Kb is the row length of A and B in
+// bytes (K for int8, K/2 for int4, K/8 for 1-bit); ldo is the distance in
+// elements between rows of the output (N for a whole product, more when the
+// launch covers a band of its columns).
 hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void *out,
                        const float *sx, const float *sw, int64_t M, int64_t N, int64_t Kb,
-                       hipStream_t s);
+                       int64_t ldo, hipStream_t s);
 // Workgroup tile and stage of a variant; bk_bytes is the K depth of a stage in bytes.
 int mfma_variant_info(int kind, int variant, int *bm, int *bn, int *bk_bytes, int *stages);
 
@@ -32,5 +34,7 @@ hipError_t launch_conv(int kind, int variant, const void *X, const void *F, int3
 // Measured selection table lookup (host only).
 int select_from_table(int dtype, int64_t M, int64_t N, int64_t K, int cu_count, int *best,
                       int *second);
+// Compute units of the current device (cached per device).
+int device_cu_count(int *cu);
 
 }  // namespace lb

@@ -143,7 +143,7 @@ template <class C, int KIND, bool CONV>
 __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, void *__restrict__ out,
     const float *__restrict__ sx, const float *__restrict__ sw,
-    int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n, ConvGeom g)
+    int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n, int32_t ldo, ConvGeom g)
 {
     // Linear layer: the tile's row and column scales follow the stage ring
     // (medium and large tiles; the small tile keeps its five workgroups per CU
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     }
 
     // Epilogue: lane holds C[m][n..n+3] for each fragment.
-    const bool vec_ok = (N & 3) == 0;
+    const bool vec_ok = ((N | ldo) & 3) == 0;
     const float *lds_sx = (const float *)(smem + C::ST * C::STAGE_BYTES);
     const float *lds_sw = lds_sx + C::BM;
 #pragma unroll
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
             if constexpr (KIND == KIND_S4) v = v >> 8;
             if constexpr (KIND == KIND_B1) v = v >> 6;
             if constexpr (KIND == KIND_LINEAR) {
-                float *o = (float *)out + m * (int64_t)N + n;
+                float *o = (float *)out + m * (int64_t)ldo + n;
                 if (vec_ok) {
                     const f32x4 s = LDS_SCALES ? *(const f32x4 *)(lds_sw + (n - n0))
                                                : *(const f32x4 *)(sw + n);
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                     for (int r = 0; r < 4 && n + r < N; ++r) o[r] = ((float)v[r] * scale_m) * (LDS_SCALES ? lds_sw[n - n0 + r] : sw[n + r]);
                 }
             } else {
-                int32_t *o = (int32_t *)out + m * (int64_t)N + n;
+                int32_t *o = (int32_t *)out + m * (int64_t)ldo + n;
                 if (vec_ok) *(i32x4 *)o = v;
                 else
                     for (int r = 0; r < 4 && n + r < N; ++r) o[r] = v[r];
@@ -449,15 +449,15 @@ using L4W8 = MfmaCfg<256, 256, 64, 4, 2, 4>;   // 128 KiB
 
 template <class C, int KIND, bool CONV>
 static hipError_t launch_one(const void *A, const void *B, void *out, const float *sx,
-                             const float *sw, int64_t M, int64_t N, int64_t Kb, const ConvGeom &g,
-                             hipStream_t s)
+                             const float *sw, int64_t M, int64_t N, int64_t Kb, int64_t ldo,
+                             const ConvGeom &g, hipStream_t s)
 {
     const uint64_t tm = (uint64_t)((M + C::BM - 1) / C::BM);
     const uint64_t tn = (uint64_t)((N + C::BN - 1) / C::BN);
     if (tm * tn > 0x7FFFFFFFull) return hipErrorInvalidValue;
     hipLaunchKernelGGL((mfma_gemm_kernel<C, KIND, CONV>), dim3((uint32_t)(tm * tn)), dim3(C::NT), 0,
                        s, (const int8_t *)A, (const int8_t *)B, out, sx, sw, (int32_t)M, (int32_t)N,
-                       (int32_t)Kb, (uint32_t)tm, (uint32_t)tn, g);
+                       (int32_t)Kb, (uint32_t)tm, (uint32_t)tn, (int32_t)ldo, g);
     return hipGetLastError();
 }
 
@@ -469,40 +469,40 @@ static void info_one(int *bm, int *bn, int *bk, int *st)
 
 template <int KIND, bool CONV>
 static hipError_t dispatch(int variant, const void *A, const void *B, void *out, const float *sx,
-                           const float *sw, int64_t M, int64_t N, int64_t Kb, const ConvGeom &g,
-                           hipStream_t s)
+                           const float *sw, int64_t M, int64_t N, int64_t Kb, int64_t ldo,
+                           const ConvGeom &g, hipStream_t s)
 {
     switch (variant) {
-    case 0: return launch_one<S2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    case 1: return launch_one<S3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    case 2: return launch_one<S4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    case 3: return launch_one<M2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    case 4: return launch_one<M3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    case 5: return launch_one<M4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 0: return launch_one<S2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+    case 1: return launch_one<S3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+    case 2: return launch_one<S4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+    case 3: return launch_one<M2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+    case 4: return launch_one<M3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+    case 5: return launch_one<M4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
     default: break;
     }
     constexpr bool b1 = KIND == KIND_B1;
     switch (variant) {
-    case 6: return launch_one<std::conditional_t<b1, L2W8, L2W16>, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
-    case 7: return launch_one<L3W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, g, s);
+    case 6: return launch_one<std::conditional_t<b1, L2W8, L2W16>, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+    case 7: return launch_one<L3W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
     case 8:
         return launch_one<std::conditional_t<b1 || KIND == KIND_S4, L4W8, L4W16>, KIND, CONV>(
-            A, B, out, sx, sw, M, N, Kb, g, s);
+            A, B, out, sx, sw, M, N, Kb, ldo, g, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void *out,
                        const float *sx, const float *sw, int64_t M, int64_t N, int64_t Kb,
-                       hipStream_t s)
+                       int64_t ldo, hipStream_t s)
 {
     const ConvGeom none{};
     switch (kind) {
-    case KIND_S8: return dispatch<KIND_S8, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
-    case KIND_S4: return dispatch<KIND_S4, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
+    case KIND_S8: return dispatch<KIND_S8, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, none, s);
+    case KIND_S4: return dispatch<KIND_S4, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, none, s);
     case KIND_LINEAR:
-        return dispatch<KIND_LINEAR, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
-    case KIND_B1: return dispatch<KIND_B1, false>(variant, A, B, out, sx, sw, M, N, Kb, none, s);
+        return dispatch<KIND_LINEAR, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, none, s);
+    case KIND_B1: return dispatch<KIND_B1, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, none, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -511,8 +511,8 @@ hipError_t launch_conv(int kind, int variant, const void *X, const void *F, int3
                        int64_t M, int64_t N, int64_t Kb, const ConvGeom &g, hipStream_t s)
 {
     switch (kind) {
-    case KIND_S8: return dispatch<KIND_S8, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, g, s);
-    case KIND_S4: return dispatch<KIND_S4, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, g, s);
+    case KIND_S8: return dispatch<KIND_S8, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, N, g, s);
+    case KIND_S4: return dispatch<KIND_S4, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, N, g, s);
     default: return hipErrorInvalidValue;
     }
 }

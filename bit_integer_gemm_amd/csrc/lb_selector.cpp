@@ -89,7 +89,9 @@ bool use_mlp(int dtype)
 
 std::atomic<int> g_cu_cache[64];
 
-int device_cu_count(int *out)
+}  // namespace
+
+int lb::device_cu_count(int *out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LB_ERR_HIP;
@@ -104,6 +106,8 @@ int device_cu_count(int *out)
     *out = cu;
     return LB_OK;
 }
+
+namespace {
 
 // Nearest measured shape of the table in log2(M, N, K) space (L1 distance).
 // The table's logarithms are taken once.
@@ -178,7 +182,7 @@ int select_from_table(int dtype, int64_t M, int64_t N, int64_t K, int cu_count, 
                       int *second)
 {
     if (cu_count <= 0) {
-        int st = device_cu_count(&cu_count);
+        int st = lb::device_cu_count(&cu_count);
         if (st != LB_OK) return st;
     }
     const int mode = use_mlp(dtype) ? 1 : 0;

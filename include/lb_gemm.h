@@ -35,12 +35,19 @@
  * variant: 0..8 picks a kernel variant, index = 3*tile + (stages - 2) with tile
  *   0 = small, 1 = medium, 2 = large and stages 2, 3 or 4 (the nine templates:
  *   three tile sizes times three pipeline depths, Research results, item 2);
- *   LB_AUTO lets lb_select_variant choose for (dtype, M, N, K).
+ *   LB_AUTO lets lb_select_variant choose for (dtype, M, N, K).  For the GEMMs
+ *   and the linear layer, when that choice is a large-tile variant (one
+ *   workgroup per CU) whose last round of tiles would fill less than half the
+ *   CUs, LB_AUTO runs the product as two launches on the stream: the widest
+ *   band of leading columns of C that fills whole rounds, then the remaining
+ *   columns with the variant chosen for their own shape.  The result is the
+ *   same; only the launch count differs.
  * Errors: every call returns an lb_status and never aborts.  Checks run in this
  *   order, before any HIP call: null pointer, non-positive size, K alignment,
  *   variant range, K limit; then the launch itself (LB_ERR_HIP).
- * Thread safety: calls may come from any thread; the only shared state is the
- *   read-only selection table.
+ * Thread safety: calls may come from any thread; the shared state is the
+ *   read-only selection table and a per-device cache of the CU count; each
+ *   thread keeps its own memory of recent selections.
  */
 #ifndef LB_GEMM_H
 #define LB_GEMM_H

@@ -340,3 +340,39 @@ def test_graph_capture_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(C.cpu().numpy(), want, err_msg=f"replay {r}")
+
+
+# ---------------------------------------------------------------------------
+# automatic choice run as two launches (a band of whole rounds of large tiles,
+# then the remaining columns)
+# ---------------------------------------------------------------------------
+
+def splits(dtype_code, M, N, K):
+    """Whether the library's automatic choice runs (M, N, K) as two launches:
+    a large-tile variant whose last round of tiles fills at most half the CUs."""
+    v = lb.lb_select_variant(dtype_code, M, N, K, 0)[0]
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    T = -(-M // 256) * -(-N // 256)
+    return v >= 6 and T > cu and T % cu != 0 and 2 * (T % cu) <= cu
+
+
+@pytest.mark.parametrize("kind,M,N,K", [
+    ("s8", 4096, 4864, 4096), ("s8", 4000, 4810, 4096),
+    ("s4", 4096, 4864, 4096), ("s4", 4000, 4810, 4096),
+    ("b1", 4000, 4810, 4096),
+])
+def test_auto_split_launches_match_oracle(kind, M, N, K):
+    print(f"[parity] split {kind} {M}x{N}x{K}", flush=True)
+    code = {"s8": lb.LB_S8, "s4": lb.LB_S4, "b1": lb.LB_B1}[kind]
+    assert splits(code, M, N, K), "shape no longer exercises the two-launch path"
+    A, B = make(kind, M, N, K, 2024)
+    got = run(kind, A, B, lb.LB_AUTO, K)
+    np.testing.assert_array_equal(got, ref(kind, A, B, K))
+
+
+def test_auto_split_linear_matches_oracle():
+    M, N, K = 4000, 4810, 4096
+    assert splits(lb.LB_S8, M, N, K)
+    X, W = inputs.s8_rows(M, K, 71), inputs.s8_rows(N, K, 72)
+    sx, sw = inputs.scales(M, 73), inputs.scales(N, 74)
+    assert_rel(run_linear(X, W, sx, sw, lb.LB_AUTO), oracle.linear_s8(X, W, sx, sw))
