@@ -39,9 +39,9 @@
  *   and the linear layer, when that choice is a large-tile variant (one
  *   workgroup per CU) whose last round of tiles would fill less than half the
  *   CUs, LB_AUTO runs the product as two launches on the stream: the widest
- *   band of leading columns of C that fills whole rounds, then the remaining
- *   columns with the variant chosen for their own shape.  The result is the
- *   same; only the launch count differs.
+ *   band of leading columns (else rows) of C that fills whole rounds, then the
+ *   rest with the variant chosen for its own shape.  The result is the same;
+ *   only the launch count differs.
  * Errors: every call returns an lb_status and never aborts.  Checks run in this
  *   order, before any HIP call: null pointer, non-positive size, K alignment,
  *   variant range, K limit; then the launch itself (LB_ERR_HIP).

@@ -356,10 +356,14 @@ def splits(dtype_code, M, N, K):
     return v >= 6 and T > cu and T % cu != 0 and 2 * (T % cu) <= cu
 
 
+# Column bands (19 tile columns over 16 tile rows), and row bands (19 tile rows
+# over 16 tile columns, where no column band fills whole rounds); ragged edges.
 @pytest.mark.parametrize("kind,M,N,K", [
     ("s8", 4096, 4864, 4096), ("s8", 4000, 4810, 4096),
     ("s4", 4096, 4864, 4096), ("s4", 4000, 4810, 4096),
     ("b1", 4000, 4810, 4096),
+    ("s8", 4864, 4096, 4096), ("s8", 4810, 4000, 4096),
+    ("s4", 4810, 4000, 4096), ("b1", 4810, 4000, 4096),
 ])
 def test_auto_split_launches_match_oracle(kind, M, N, K):
     print(f"[parity] split {kind} {M}x{N}x{K}", flush=True)
@@ -370,8 +374,9 @@ def test_auto_split_launches_match_oracle(kind, M, N, K):
     np.testing.assert_array_equal(got, ref(kind, A, B, K))
 
 
-def test_auto_split_linear_matches_oracle():
-    M, N, K = 4000, 4810, 4096
+@pytest.mark.parametrize("M,N", [(4000, 4810), (4810, 4000)])
+def test_auto_split_linear_matches_oracle(M, N):
+    K = 4096
     assert splits(lb.LB_S8, M, N, K)
     X, W = inputs.s8_rows(M, K, 71), inputs.s8_rows(N, K, 72)
     sx, sw = inputs.scales(M, 73), inputs.scales(N, 74)
