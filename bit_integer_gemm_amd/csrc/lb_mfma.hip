@@ -428,7 +428,13 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
 using S2 = MfmaCfg<64, 64, 128, 2, 2, 2>;     // 32 KiB
 using S3 = MfmaCfg<64, 64, 128, 2, 2, 3>;     // 48 KiB
 using S4 = MfmaCfg<64, 64, 128, 2, 2, 4>;     // 64 KiB
-using M2 = MfmaCfg<128, 128, 128, 2, 2, 2>;   // 64 KiB
+// The 2-stage medium tile runs 8 waves of 32x64 (two workgroups per CU): 3-16%
+// faster than 4 waves of 64x64 on most shapes that choose it (4% slower at
+// 1024 x 1024 x 4096); the 3- and 4-stage medium tiles lose with 8 waves and
+// keep 4, as does the int4 convolution (its window gather, spread over twice
+// the waves, made the 3x3 layer over 14x14x256 6% slower).
+using M2 = MfmaCfg<128, 128, 128, 4, 2, 2>;   // 64 KiB
+using M2W4 = MfmaCfg<128, 128, 128, 2, 2, 2>; // 64 KiB
 using M3 = MfmaCfg<128, 128, 64, 2, 2, 3>;    // 48 KiB
 using M4 = MfmaCfg<128, 128, 64, 2, 2, 4>;    // 64 KiB
 // Large tile: 16 waves of 64x64 (L2W16, L4W16) or 8 waves of 64x128 (W8).
@@ -476,7 +482,9 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     case 0: return launch_one<S2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
     case 1: return launch_one<S3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
     case 2: return launch_one<S4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
-    case 3: return launch_one<M2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+    case 3:
+        return launch_one<std::conditional_t<CONV && KIND == KIND_S4, M2W4, M2>, KIND, CONV>(
+            A, B, out, sx, sw, M, N, Kb, ldo, g, s);
     case 4: return launch_one<M3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
     case 5: return launch_one<M4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
     default: break;
