@@ -423,7 +423,8 @@ def main():
 
     if not args.only and not args.no_extras:
         extras = {}
-        for w in ("s4_gemm_4096", "s8_gemm_4096", "b1_gemm_4096x4096x8192", "s8_linear_8192x11008x4096"):
+        for w in ("s4_gemm_4096", "s8_gemm_4096", "b1_gemm_4096x4096x8192", "s8_linear_8192x11008x4096",
+                  "s8_gemm_256"):
             extras[w] = measure(w, torch, lb)
         for w in CONV_LAYERS:
             extras[w] = measure_conv(w, torch, lb)
