@@ -12,10 +12,14 @@ enum { KIND_S8 = 0, KIND_S4 = 1, KIND_LINEAR = 2, KIND_B1 = 3 };
 // 1-bit GEMM on weighted bit planes).  Kb is the row length of A and B in
 // bytes (K for int8, K/2 for int4, K/8 for 1-bit); ldo is the distance in
 // elements between rows of the output (N for a whole product, more when the
-// launch covers a band of its columns).
+// launch covers a band of its columns).  ksplit < Kb (integer GEMMs only, a
+// multiple of the variant's stage depth) runs ceil(Kb / ksplit) bands of K in
+// one grid, each adding its partial sums into C, which must hold zeros.
 hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void *out,
                        const float *sx, const float *sw, int64_t M, int64_t N, int64_t Kb,
-                       int64_t ldo, hipStream_t s);
+                       int64_t ldo, int64_t ksplit, hipStream_t s);
+// Zero n int32 values on the stream (a kernel, not a memset).
+hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t s);
 // Workgroup tile and stage of a variant; bk_bytes is the K depth of a stage in bytes.
 int mfma_variant_info(int kind, int variant, int *bm, int *bn, int *bk_bytes, int *stages);
 

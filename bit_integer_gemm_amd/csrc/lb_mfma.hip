@@ -59,6 +59,7 @@
 //    bytes per pixel are a multiple of 64, so one 64-byte K block sits inside
 //    a single tap; pieces that fall in the zero padding (or past M or K) get
 //    an offset with bit 31 set, beyond the buffer range, and load zero.
+#include <algorithm>
 #include <type_traits>
 
 #include "lb_device.hpp"
@@ -143,7 +144,8 @@ template <class C, int KIND, bool CONV>
 __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, void *__restrict__ out,
     const float *__restrict__ sx, const float *__restrict__ sw,
-    int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n, int32_t ldo, ConvGeom g)
+    int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n, int32_t ldo,
+    int32_t ksplit, ConvGeom g)
 {
     // Linear layer: the tile's row and column scales follow the stage ring
     // (medium and large tiles; the small tile keeps its five workgroups per CU
@@ -161,10 +163,17 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     tile_of_block(blockIdx.x, tiles_m, tiles_n, 8u, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
-    const int8_t *Ab = A + m0 * Kb;
-    const int8_t *Bb = B + n0 * Kb;
-    const int64_t a_bytes = (int64_t)(M - m0) * Kb;
-    const int64_t b_bytes = (int64_t)(N - n0) * Kb;
+    // Split K: workgroup row blockIdx.y sums K bytes [kbeg, kbeg + klen) of the
+    // product and adds its partial result into C (which the host zeroed); a
+    // grid of one row covers all of K (ksplit = Kb) and stores.  Kb stays the
+    // row stride of A and B.
+    const int64_t kbeg = (int64_t)blockIdx.y * ksplit;
+    const int32_t klen = (int32_t)((int64_t)Kb - kbeg < ksplit ? (int64_t)Kb - kbeg : (int64_t)ksplit);
+    const bool accumulate = gridDim.y > 1;
+    const int8_t *Ab = A + m0 * Kb + kbeg;
+    const int8_t *Bb = B + n0 * Kb + kbeg;
+    const int64_t a_bytes = (int64_t)(M - m0) * Kb - kbeg;
+    const int64_t b_bytes = (int64_t)(N - n0) * Kb - kbeg;
 
     // Per-copy lane offsets inside the tile (constant over K).
     uint32_t voff[C::NDMA];
@@ -254,8 +263,8 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-    const int64_t nk = ((int64_t)Kb + C::BK - 1) / C::BK;
-    const bool k_tail = (Kb % C::BK) != 0;
+    const int64_t nk = ((int64_t)klen + C::BK - 1) / C::BK;
+    const bool k_tail = (klen % C::BK) != 0;
 
     // Linear layer: wave 0 copies sx[m0 .. m0+BM) and sw[n0 .. n0+BN) into LDS
     // ahead of the first stage (entries past M or N read as zero).  These copies
@@ -283,7 +292,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
         wait_outstanding<C::NDMA, C::ST>((int)(after < C::ST - 2 ? after : C::ST - 2));
         char *stage = smem + slot * C::STAGE_BYTES;
         if (k_tail && kt == nk - 1) {
-            zero_k_tail<C>(stage, lane, wave, kt * C::BK, Kb);
+            zero_k_tail<C>(stage, lane, wave, kt * C::BK, klen);
             barrier_lds();
         }
         if constexpr (LATE_COPIES)
@@ -408,9 +417,13 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                 }
             } else {
                 int32_t *o = (int32_t *)out + m * (int64_t)ldo + n;
-                if (vec_ok) *(i32x4 *)o = v;
-                else
+                if (accumulate) {
+                    for (int r = 0; r < 4 && n + r < N; ++r) atomicAdd(o + r, v[r]);
+                } else if (vec_ok) {
+                    *(i32x4 *)o = v;
+                } else {
                     for (int r = 0; r < 4 && n + r < N; ++r) o[r] = v[r];
+                }
             }
         }
     }
@@ -456,14 +469,17 @@ using L4W8 = MfmaCfg<256, 256, 64, 4, 2, 4>;   // 128 KiB
 template <class C, int KIND, bool CONV>
 static hipError_t launch_one(const void *A, const void *B, void *out, const float *sx,
                              const float *sw, int64_t M, int64_t N, int64_t Kb, int64_t ldo,
-                             const ConvGeom &g, hipStream_t s)
+                             int64_t ksplit, const ConvGeom &g, hipStream_t s)
 {
     const uint64_t tm = (uint64_t)((M + C::BM - 1) / C::BM);
     const uint64_t tn = (uint64_t)((N + C::BN - 1) / C::BN);
     if (tm * tn > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((mfma_gemm_kernel<C, KIND, CONV>), dim3((uint32_t)(tm * tn)), dim3(C::NT), 0,
-                       s, (const int8_t *)A, (const int8_t *)B, out, sx, sw, (int32_t)M, (int32_t)N,
-                       (int32_t)Kb, (uint32_t)tm, (uint32_t)tn, (int32_t)ldo, g);
+    if (ksplit <= 0 || ksplit > Kb) ksplit = Kb;
+    if (ksplit < Kb && (CONV || KIND == KIND_LINEAR || ksplit % C::BK != 0)) return hipErrorInvalidValue;
+    const uint32_t nsplit = (uint32_t)((Kb + ksplit - 1) / ksplit);
+    hipLaunchKernelGGL((mfma_gemm_kernel<C, KIND, CONV>), dim3((uint32_t)(tm * tn), nsplit), dim3(C::NT),
+                       0, s, (const int8_t *)A, (const int8_t *)B, out, sx, sw, (int32_t)M, (int32_t)N,
+                       (int32_t)Kb, (uint32_t)tm, (uint32_t)tn, (int32_t)ldo, (int32_t)ksplit, g);
     return hipGetLastError();
 }
 
@@ -476,41 +492,58 @@ static void info_one(int *bm, int *bn, int *bk, int *st)
 template <int KIND, bool CONV>
 static hipError_t dispatch(int variant, const void *A, const void *B, void *out, const float *sx,
                            const float *sw, int64_t M, int64_t N, int64_t Kb, int64_t ldo,
-                           const ConvGeom &g, hipStream_t s)
+                           int64_t ksplit, const ConvGeom &g, hipStream_t s)
 {
     switch (variant) {
-    case 0: return launch_one<S2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
-    case 1: return launch_one<S3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
-    case 2: return launch_one<S4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+    case 0: return launch_one<S2, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+    case 1: return launch_one<S3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+    case 2: return launch_one<S4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     case 3:
         return launch_one<std::conditional_t<CONV && KIND == KIND_S4, M2W4, M2>, KIND, CONV>(
-            A, B, out, sx, sw, M, N, Kb, ldo, g, s);
-    case 4: return launch_one<M3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
-    case 5: return launch_one<M4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+            A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+    case 4: return launch_one<M3, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+    case 5: return launch_one<M4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     default: break;
     }
     constexpr bool b1 = KIND == KIND_B1;
     switch (variant) {
-    case 6: return launch_one<std::conditional_t<b1, L2W8, L2W16>, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
-    case 7: return launch_one<L3W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+    case 6: return launch_one<std::conditional_t<b1, L2W8, L2W16>, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+    case 7: return launch_one<L3W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     case 8:
         return launch_one<std::conditional_t<b1 || KIND == KIND_S4, L4W8, L4W16>, KIND, CONV>(
-            A, B, out, sx, sw, M, N, Kb, ldo, g, s);
+            A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     default: return hipErrorInvalidValue;
     }
 }
 
+// Zero n int32 values (the output of a split-K product, before its partial
+// sums are added).  A kernel rather than hipMemsetAsync, so that a captured
+// graph holds only kernel nodes.
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t *__restrict__ p, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) p[i] = 0;
+}
+
+hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+    hipLaunchKernelGGL(zero_i32_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void *out,
                        const float *sx, const float *sw, int64_t M, int64_t N, int64_t Kb,
-                       int64_t ldo, hipStream_t s)
+                       int64_t ldo, int64_t ksplit, hipStream_t s)
 {
     const ConvGeom none{};
     switch (kind) {
-    case KIND_S8: return dispatch<KIND_S8, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, none, s);
-    case KIND_S4: return dispatch<KIND_S4, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, none, s);
+    case KIND_S8: return dispatch<KIND_S8, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, ksplit, none, s);
+    case KIND_S4: return dispatch<KIND_S4, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, ksplit, none, s);
     case KIND_LINEAR:
-        return dispatch<KIND_LINEAR, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, none, s);
-    case KIND_B1: return dispatch<KIND_B1, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, none, s);
+        return dispatch<KIND_LINEAR, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, ksplit, none, s);
+    case KIND_B1: return dispatch<KIND_B1, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, ksplit, none, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -519,8 +552,8 @@ hipError_t launch_conv(int kind, int variant, const void *X, const void *F, int3
                        int64_t M, int64_t N, int64_t Kb, const ConvGeom &g, hipStream_t s)
 {
     switch (kind) {
-    case KIND_S8: return dispatch<KIND_S8, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, N, g, s);
-    case KIND_S4: return dispatch<KIND_S4, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, N, g, s);
+    case KIND_S8: return dispatch<KIND_S8, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, N, Kb, g, s);
+    case KIND_S4: return dispatch<KIND_S4, true>(variant, X, F, Y, nullptr, nullptr, M, N, Kb, N, Kb, g, s);
     default: return hipErrorInvalidValue;
     }
 }

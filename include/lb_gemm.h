@@ -40,8 +40,11 @@
  *   workgroup per CU) whose last round of tiles would fill less than half the
  *   CUs, LB_AUTO runs the product as two launches on the stream: the widest
  *   band of leading columns (else rows) of C that fills whole rounds, then the
- *   rest with the variant chosen for its own shape.  The result is the same;
- *   only the launch count differs.
+ *   rest with the variant chosen for its own shape.  For the integer GEMMs,
+ *   when the chosen variant's tiles fill at most a quarter of the CUs and K is
+ *   long, LB_AUTO zeroes C with a kernel and cuts K into bands that add their
+ *   exact partial sums into C.  Either way the result is the same (integer
+ *   sums do not depend on their order); only the launches differ.
  * Errors: every call returns an lb_status and never aborts.  Checks run in this
  *   order, before any HIP call: null pointer, non-positive size, K alignment,
  *   variant range, K limit; then the launch itself (LB_ERR_HIP).

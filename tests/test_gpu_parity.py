@@ -381,3 +381,60 @@ def test_auto_split_linear_matches_oracle(M, N):
     X, W = inputs.s8_rows(M, K, 71), inputs.s8_rows(N, K, 72)
     sx, sw = inputs.scales(M, 73), inputs.scales(N, 74)
     assert_rel(run_linear(X, W, sx, sw, lb.LB_AUTO), oracle.linear_s8(X, W, sx, sw))
+
+
+# ---------------------------------------------------------------------------
+# automatic choice with K cut into bands (few tiles, long K): each band adds its
+# exact partial sums into C
+# ---------------------------------------------------------------------------
+
+MIN_BAND = {"s8": 1024, "s4": 512, "b1": 256}
+KB_PER = {"s8": 1, "s4": 2, "b1": 8}   # elements per byte
+
+
+def k_bands(kind, M, N, K):
+    """Number of K bands the library's automatic choice uses for (M, N, K)."""
+    code = {"s8": lb.LB_S8, "s4": lb.LB_S4, "b1": lb.LB_B1}[kind]
+    v = lb.lb_select_variant(code, M, N, K, 0)[0]
+    info = lb.lb_variant_info(code, v)
+    tm, tn = info["tile_m"], info["tile_n"]
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = -(-M // tm) * -(-N // tn)
+    kb = K // KB_PER[kind]
+    if 4 * tiles > cu:
+        return 1
+    S = min(cu // tiles, 16, kb // MIN_BAND[kind], (1 << 19) // (M * N), 64 * K // (M * N))
+    if S < 2:
+        return 1
+    length = -(-(-(-kb // S)) // 128) * 128
+    return -(-kb // length)
+
+
+@pytest.mark.parametrize("kind,M,N,K", [
+    ("s8", 64, 64, 8192), ("s8", 100, 70, 4112), ("s8", 256, 512, 16384), ("s8", 1, 1, 2048),
+    ("s4", 64, 64, 8192), ("s4", 100, 70, 4128),
+    ("b1", 64, 64, 32768), ("b1", 100, 70, 16512),
+])
+def test_auto_k_bands_match_oracle(kind, M, N, K):
+    bands = k_bands(kind, M, N, K)
+    print(f"[parity] k bands {kind} {M}x{N}x{K}: {bands}", flush=True)
+    assert bands >= 2, "shape no longer exercises the K-band path"
+    A, B = make(kind, M, N, K, 3030)
+    np.testing.assert_array_equal(run(kind, A, B, lb.LB_AUTO, K), ref(kind, A, B, K))
+
+
+def test_auto_k_bands_extreme_values():
+    """Largest-magnitude operands at the largest K, K cut into bands: every
+    band's partial sum and every running total of C stays exact."""
+    M, N = 33, 47
+    K = 131056
+    assert k_bands("s8", M, N, K) >= 2
+    A = np.full((M, K), -128, np.int8)
+    got = run("s8", A, np.full((N, K), -128, np.int8), lb.LB_AUTO)
+    assert (got == 16384 * K).all()
+    got = run("s8", A, np.full((N, K), 127, np.int8), lb.LB_AUTO)
+    assert (got == -16256 * K).all()
+    K4 = 131040
+    A4 = inputs.pack_s4(np.full((M, K4), -8, np.int8))
+    got = run("s4", A4, inputs.pack_s4(np.full((N, K4), 7, np.int8)), lb.LB_AUTO)
+    assert (got == -56 * K4).all()
