@@ -438,3 +438,36 @@ def test_auto_k_bands_extreme_values():
     A4 = inputs.pack_s4(np.full((M, K4), -8, np.int8))
     got = run("s4", A4, inputs.pack_s4(np.full((N, K4), 7, np.int8)), lb.LB_AUTO)
     assert (got == -56 * K4).all()
+
+
+@pytest.mark.parametrize("kind,M,N,K", [("s8", 64, 64, 8192), ("s8", 4000, 4810, 4096)])
+def test_graph_capture_of_automatic_launches(kind, M, N, K):
+    """The automatic path's extra launches (the zeroing of C before K bands, or
+    the second launch of a two-launch split) captured into a HIP graph: every
+    replay, with eager work and a clobbered C in between, reproduces the oracle."""
+    if (M, N) == (64, 64):
+        assert k_bands(kind, M, N, K) >= 2
+    else:
+        assert splits(lb.LB_S8, M, N, K)
+    A, B = make(kind, M, N, K, 5151)
+    dA, dB = to_dev(A), to_dev(B)
+    want = oracle.gemm_s8(A, B)
+    C = torch.zeros(M, N, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lb.lb_gemm_s8(dA, dB, C, lb.LB_AUTO)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lb.lb_gemm_s8(dA, dB, C, lb.LB_AUTO)
+    x = to_dev(inputs.s8_rows(256, 1024, 5152))
+    other = torch.empty(256, 256, dtype=torch.int32, device="cuda")
+    for r in range(3):
+        C.fill_(12345)
+        lb.lb_gemm_s8(x, x, other, lb.LB_AUTO)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(C.cpu().numpy(), want, err_msg=f"replay {r}")
