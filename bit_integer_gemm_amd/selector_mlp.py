@@ -50,6 +50,8 @@ def load_sweep(paths):
     for p in paths:
         for line in open(p):
             r = json.loads(line)
+            if r["variant"] == "auto":   # the library's own choice, not one of the nine
+                continue
             out.setdefault(r["dtype"], {}).setdefault((r["M"], r["N"], r["K"]), [None] * 9)[r["variant"]] = r["sec"]
     return {d: {k: v for k, v in s.items() if None not in v} for d, s in out.items()}
 

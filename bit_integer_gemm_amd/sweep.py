@@ -140,6 +140,8 @@ def run_sweep(dtype, out_path, Ms=None, Ns=None, Ks=None, check=True, log=print)
         for M in Ms:
             for N in Ns:
                 todo = [v for v in range(9) if (M, N, K, v) not in done]
+                if (M, N, K, "auto") not in done:
+                    todo.append("auto")
                 if not todo:
                     continue
                 A, B = dA[:M], dB[:N]
@@ -151,13 +153,16 @@ def run_sweep(dtype, out_path, Ms=None, Ns=None, Ks=None, check=True, log=print)
                 line_t = []
                 sel = lb.lb_select_variant(DTYPES[dtype], M, N, K, 0)
                 for v in todo:
-                    t, reps = time_calls(lambda: call(A, B, C, v), torch)
+                    # "auto": the library's own choice (LB_AUTO), which may add a
+                    # two-launch split or K bands on top of the selected variant
+                    vv = lb.LB_AUTO if v == "auto" else v
+                    t, reps = time_calls(lambda: call(A, B, C, vv), torch)
                     agree = bool(torch.equal(C, ref)) if check else None
                     rec = {"dtype": dtype, "M": M, "N": N, "K": K, "variant": v, "sec": t, "reps": reps,
                            "tops": 2.0 * M * N * K / t / 1e12, "agrees_with_default": agree,
                            "selected": sel[0], "second": sel[1]}
                     f.write(json.dumps(rec) + "\n")
-                    line_t.append(f"v{v}:{t * 1e6:.1f}")
+                    line_t.append(f"{'' if v == 'auto' else 'v'}{v}:{t * 1e6:.1f}")
                     if check and not agree:
                         raise RuntimeError(f"variant {v} disagrees with the default at {dtype} {M}x{N}x{K}")
                 f.flush()
@@ -168,11 +173,15 @@ def run_sweep(dtype, out_path, Ms=None, Ns=None, Ks=None, check=True, log=print)
     f.close()
 
 
-def load_records(paths):
+def load_records(paths, auto=False):
+    """Timings keyed by (dtype, M, N, K, variant): the nine variants, or with
+    auto=True the records of the library's own choice (variant "auto")."""
     recs = {}
     for p in paths:
         for line in open(p):
             r = json.loads(line)
+            if (r["variant"] == "auto") != auto:
+                continue
             recs[(r["dtype"], r["M"], r["N"], r["K"], r["variant"])] = r
     return recs
 
@@ -220,6 +229,7 @@ def evaluate(table_files, eval_files, eps=EPS, default=DEFAULT):
     lb_select_variant returned) and the second run's timings as truth.
     """
     recs = load_records(eval_files)
+    autos = {k[:4]: r["sec"] for k, r in load_records(eval_files, auto=True).items()}
     shapes = {}
     sel = {}
     for (d, M, N, K, v), r in recs.items():
@@ -247,7 +257,19 @@ def evaluate(table_files, eval_files, eps=EPS, default=DEFAULT):
     top1 = sum(1 for r in rows if r["sel"] == r["best"]) / n
     top2 = sum(1 for r in rows if r["best"] in (r["sel"], r["second"])) / n
     top1e = sum(1 for r in rows if near(r, r["sel"])) / n
-    return {
+    auto = {}
+    ar = [(r, autos[r["shape"]]) for r in rows if r["shape"] in autos]
+    if ar:
+        sp_a_def = [r["t"][default] / ta for r, ta in ar]
+        sp_a_sel = [r["t"][r["sel"]] / ta for r, ta in ar]
+        sp_a_best = [r["t"][r["best"]] / ta for r, ta in ar]
+        auto = {"automatic_path": {
+            "shapes": len(ar),
+            "speedup_vs_default": {"geomean": gm(sp_a_def), "max": max(sp_a_def), "min": min(sp_a_def)},
+            "speedup_vs_selected_variant": {"geomean": gm(sp_a_sel), "max": max(sp_a_sel), "min": min(sp_a_sel)},
+            "speedup_vs_fastest_variant": {"geomean": gm(sp_a_best), "max": max(sp_a_best), "min": min(sp_a_best)},
+            "slower_than_default": sum(1 for x in sp_a_def if x < 1 / (1 + eps))}}
+    return {**auto,
         "shapes": n, "eps": eps, "default_variant": default,
         "violations_slower_than_default": len(viol),
         "violation_shapes": [r["shape"] for r in viol],

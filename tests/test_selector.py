@@ -170,3 +170,32 @@ def test_repeated_queries_and_mode_switches_agree():
         assert got in {(e[4], e[5]) for e in cand if abs(dist(e) - best) < 1e-12}
     # the two modes really differ somewhere, so the test can see a stale answer
     assert any(table[s] != mlp[s] for s in shapes)
+
+
+def test_sweep_records_of_the_automatic_path(tmp_path):
+    """Sweep files may hold records of the library's own choice (variant
+    "auto"): labels and the classifier's loader ignore them, and the evaluation
+    reports the automatic path against the default and the selected variant."""
+    import json
+    from bit_integer_gemm_amd import selector_mlp, sweep
+    p = tmp_path / "run.jsonl"
+    recs = []
+    for M in (64, 128):
+        times = [10.0] * 9
+        times[2] = 4.0
+        for v, t in enumerate(times):
+            recs.append({"dtype": "s8", "M": M, "N": 64, "K": 256, "variant": v, "sec": t,
+                         "selected": 2, "second": 0})
+        recs.append({"dtype": "s8", "M": M, "N": 64, "K": 256, "variant": "auto", "sec": 2.0,
+                     "selected": 2, "second": 0})
+    p.write_text("\n".join(json.dumps(r) for r in recs) + "\n")
+    lab = sweep.labels(sweep.load_records([str(p)]))
+    assert lab[("s8", 64, 64, 256)][:2] == (2, 0)
+    assert set(selector_mlp.load_sweep([str(p)])["s8"]) == {(64, 64, 256), (128, 64, 256)}
+    rep = sweep.evaluate(None, [str(p)])
+    assert rep["shapes"] == 2 and rep["violations_slower_than_default"] == 0
+    a = rep["automatic_path"]
+    assert a["shapes"] == 2
+    assert abs(a["speedup_vs_default"]["geomean"] - 5.0) < 1e-9
+    assert abs(a["speedup_vs_selected_variant"]["geomean"] - 2.0) < 1e-9
+    assert a["slower_than_default"] == 0
