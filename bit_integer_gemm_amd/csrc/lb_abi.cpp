@@ -77,15 +77,18 @@ int plan_parts(int dtype, int variant, int64_t M, int64_t N, int64_t K, Part *pa
 // one output element.
 // Split K.  A product whose tiles fill at most a quarter of the CUs (small
 // M x N) leaves the chip mostly idle however long K is.  An automatic choice
-// for an integer GEMM then cuts K into S bands of whole stages, zeroes C and
-// runs all bands in one grid, each adding its exact int32 partial sums into C
+// for an integer GEMM may then cut K into S bands of whole stages, zero C and
+// run all bands in one grid, each adding its exact int32 partial sums into C
 // with atomic adds; integer addition makes the result independent of their
-// order.  S is at most CUs / tiles and 16, keeps each band at least min_band
-// bytes long, keeps M*N*S (the atomic adds) within 2^19, and is at most
-// 64 K / (M N) for K in elements: the adds cost ~12 ps each across the chip
-// (1M took 12 us) and must cost less than the bands save (measured: 2 bands of
-// 512 x 512 x 8192 1.21x faster, of 64 x 4096 x 4096 0.91x, which the last
-// bound excludes).  Returns S (1: no split) and the band length in bytes.
+// order.  S comes from a cost model fitted to measurements on MI355X: a
+// one-round product takes about alpha ns per element of K (2.5 int8, 2.3 int4,
+// 1.25 1-bit); S bands take alpha K / S, plus ~3 us for the zeroing launch,
+// plus ~15 ps per atomic add (M N S of them).  The S (2..16, at most
+// CUs / tiles and whole 128-byte stages) with the lowest estimate is used when
+// that estimate beats alpha K by 1.3x (measured: int8 64 x 64 x 8192 2.9x
+// faster, 1-bit 64 x 64 x 32768 4.9x; the model declines 64 x 4096 x 4096 and
+// 1-bit 4096 x 64 x 8192, where bands lost 9% and 47%).  Returns S (1: no
+// split) and the band length in bytes.
 int plan_ksplit(int kind, int variant, int64_t M, int64_t N, int64_t kb, int64_t *band)
 {
     *band = kb;
@@ -95,16 +98,21 @@ int plan_ksplit(int kind, int variant, int64_t M, int64_t N, int64_t kb, int64_t
     if (lb::device_cu_count(&cu) != LB_OK || cu <= 0) return 1;
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     if (4 * tiles > cu) return 1;
-    const int64_t min_band = kind == lb::KIND_S8 ? 1024 : kind == lb::KIND_S4 ? 512 : 256;
-    int64_t S = cu / tiles;
-    if (S > 16) S = 16;
-    if (S > kb / min_band) S = kb / min_band;
-    if (S > (int64_t(1) << 19) / (M * N)) S = (int64_t(1) << 19) / (M * N);
-    const int64_t k_elems = kb * (kind == lb::KIND_S8 ? 1 : kind == lb::KIND_S4 ? 2 : 8);
-    if (S > 64 * k_elems / (M * N)) S = 64 * k_elems / (M * N);
-    if (S < 2) return 1;
+    const int per_byte = kind == lb::KIND_S8 ? 1 : kind == lb::KIND_S4 ? 2 : 8;
+    const double alpha = kind == lb::KIND_S8 ? 2.5 : kind == lb::KIND_S4 ? 2.3 : 1.25;
+    const double t0 = alpha * (double)kb * per_byte;
     const int64_t step = 128;  // a multiple of every variant's stage depth
-    const int64_t len = ((kb + S - 1) / S + step - 1) / step * step;
+    int64_t smax = cu / tiles;
+    if (smax > 16) smax = 16;
+    if (smax > kb / step) smax = kb / step;
+    int best = 1;
+    double best_t = t0;
+    for (int64_t S = 2; S <= smax; ++S) {
+        const double t = t0 / (double)S + 3000.0 + 0.015 * (double)M * (double)N * (double)S;
+        if (t < best_t) { best_t = t; best = (int)S; }
+    }
+    if (best < 2 || best_t * 1.3 > t0) return 1;
+    const int64_t len = ((kb + best - 1) / best + step - 1) / step * step;
     const int64_t bands = (kb + len - 1) / len;
     if (bands < 2) return 1;
     *band = len;

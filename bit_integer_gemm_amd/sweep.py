@@ -154,13 +154,18 @@ def run_sweep(dtype, out_path, Ms=None, Ns=None, Ks=None, check=True, log=print)
                 sel = lb.lb_select_variant(DTYPES[dtype], M, N, K, 0)
                 for v in todo:
                     # "auto": the library's own choice (LB_AUTO), which may add a
-                    # two-launch split or K bands on top of the selected variant
+                    # two-launch split or K bands on top of the selected variant;
+                    # the selected variant is timed again right before it, so
+                    # that the two compare at the same clocks
                     vv = lb.LB_AUTO if v == "auto" else v
+                    t_adj = time_calls(lambda: call(A, B, C, sel[0]), torch)[0] if v == "auto" else None
                     t, reps = time_calls(lambda: call(A, B, C, vv), torch)
                     agree = bool(torch.equal(C, ref)) if check else None
                     rec = {"dtype": dtype, "M": M, "N": N, "K": K, "variant": v, "sec": t, "reps": reps,
                            "tops": 2.0 * M * N * K / t / 1e12, "agrees_with_default": agree,
                            "selected": sel[0], "second": sel[1]}
+                    if t_adj is not None:
+                        rec["selected_sec_adjacent"] = t_adj
                     f.write(json.dumps(rec) + "\n")
                     line_t.append(f"{'' if v == 'auto' else 'v'}{v}:{t * 1e6:.1f}")
                     if check and not agree:
@@ -229,7 +234,9 @@ def evaluate(table_files, eval_files, eps=EPS, default=DEFAULT):
     lb_select_variant returned) and the second run's timings as truth.
     """
     recs = load_records(eval_files)
-    autos = {k[:4]: r["sec"] for k, r in load_records(eval_files, auto=True).items()}
+    auto_recs = load_records(eval_files, auto=True)
+    autos = {k[:4]: r["sec"] for k, r in auto_recs.items()}
+    adjacent = {k[:4]: r["selected_sec_adjacent"] for k, r in auto_recs.items() if "selected_sec_adjacent" in r}
     shapes = {}
     sel = {}
     for (d, M, N, K, v), r in recs.items():
@@ -261,7 +268,9 @@ def evaluate(table_files, eval_files, eps=EPS, default=DEFAULT):
     ar = [(r, autos[r["shape"]]) for r in rows if r["shape"] in autos]
     if ar:
         sp_a_def = [r["t"][default] / ta for r, ta in ar]
-        sp_a_sel = [r["t"][r["sel"]] / ta for r, ta in ar]
+        # against the selected variant timed right before the automatic path
+        # when the run has it (same clocks), else its own timing in the run
+        sp_a_sel = [adjacent.get(r["shape"], r["t"][r["sel"]]) / ta for r, ta in ar]
         sp_a_best = [r["t"][r["best"]] / ta for r, ta in ar]
         auto = {"automatic_path": {
             "shapes": len(ar),

@@ -388,12 +388,13 @@ def test_auto_split_linear_matches_oracle(M, N):
 # exact partial sums into C
 # ---------------------------------------------------------------------------
 
-MIN_BAND = {"s8": 1024, "s4": 512, "b1": 256}
 KB_PER = {"s8": 1, "s4": 2, "b1": 8}   # elements per byte
+ALPHA = {"s8": 2.5, "s4": 2.3, "b1": 1.25}
 
 
 def k_bands(kind, M, N, K):
-    """Number of K bands the library's automatic choice uses for (M, N, K)."""
+    """Number of K bands the library's automatic choice uses for (M, N, K):
+    the cost model of the header's split-K rule, restated."""
     code = {"s8": lb.LB_S8, "s4": lb.LB_S4, "b1": lb.LB_B1}[kind]
     v = lb.lb_select_variant(code, M, N, K, 0)[0]
     info = lb.lb_variant_info(code, v)
@@ -403,10 +404,16 @@ def k_bands(kind, M, N, K):
     kb = K // KB_PER[kind]
     if 4 * tiles > cu:
         return 1
-    S = min(cu // tiles, 16, kb // MIN_BAND[kind], (1 << 19) // (M * N), 64 * K // (M * N))
-    if S < 2:
+    t0 = ALPHA[kind] * K
+    smax = min(cu // tiles, 16, kb // 128)
+    best, best_t = 1, t0
+    for S in range(2, smax + 1):
+        t = t0 / S + 3000.0 + 0.015 * M * N * S
+        if t < best_t:
+            best, best_t = S, t
+    if best < 2 or best_t * 1.3 > t0:
         return 1
-    length = -(-(-(-kb // S)) // 128) * 128
+    length = -(-(-(-kb // best)) // 128) * 128
     return -(-kb // length)
 
 
