@@ -62,12 +62,22 @@ CONV_LAYERS = {
 KERNEL_SOURCES = ("lb_device.hpp", "lb_internal.hpp", "lb_mfma.hip")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (string literals in these
+    files hold no comment markers), so that a comment edit keeps the hash."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
 def kernel_source_sha() -> str:
+    """Hash of the device code (comments ignored); counter profiles carry it."""
     d = os.path.join(ROOT, "bit_integer_gemm_amd", "csrc")
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         h.update(f.encode())
-        h.update(open(os.path.join(d, f), "rb").read())
+        h.update(_code_only(open(os.path.join(d, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

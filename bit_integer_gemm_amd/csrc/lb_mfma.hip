@@ -50,6 +50,10 @@
 //    epilogue divides by 64.
 //  * Rows past M or N read as zero through the buffer range check; a partial
 //    last K stage has its out-of-range A pieces zeroed in LDS before use.
+//  * A launch may cover a band of C: the output's row stride is an argument
+//    (a band of columns), and a grid with several rows of workgroups splits K
+//    (row y sums bytes [y*ksplit, (y+1)*ksplit) of K and adds its exact
+//    partial sums into a zeroed C with atomic adds; integer GEMMs only).
 //  * Convolution (the im2win convolution summary, gist.science paper
 //    2608.20725, method: NHWC images, a window per output) runs through the
 //    same kernel: row r of A is output pixel r and its K axis walks the filter
