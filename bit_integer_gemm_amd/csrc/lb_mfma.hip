@@ -433,6 +433,274 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     }
 }
 
+// ---- large int8 tile on four waves --------------------------------------
+// The 2-stage large variant of the int8 GEMM and the int8 linear layer: a
+// 256x256 tile on four waves (one per SIMD) of 128x128, all 256 int32
+// accumulators of a lane in AGPRs.  Per workgroup, per 64 K-bytes: 64 KiB of
+// LDS fragment reads for 256 MFMAs, against 128 KiB for sixteen waves of
+// 64x64.
+//  * Two LDS super-stages of 128 K-bytes (64 KiB each: 256 A rows, 256 B rows)
+//    form the 2-stage ring.  A 2 KiB block holds 16 rows x 128 bytes as two
+//    1 KiB halves of 8 rows; row r's 16-byte chunk c sits at
+//    (r/8)*1024 + (r%8)*128 + 16*(c ^ (r%8)).  One copy fills one half: lane
+//    i reads chunk (i%8) ^ (i/8) of row i/8, so each 8 lanes read one whole
+//    128-byte line.  The fragment read of K half h (lane l: row l%16, chunk
+//    l/16 + 4h) is conflict-free: the 8 lanes served together hold rows
+//    r..r+7 of one half, at distinct slots (c + 4h) ^ (r%8).
+//  * Block t (64 K-bytes) is half t%2 of super-stage t/2.  Each block runs
+//    its MFMAs in two halves (rows 0-3, then 4-7 of the wave's 8x8 fragment
+//    grid); the next block's 16 fragments are read between the second half's
+//    MFMAs, so LDS latency stays under the matrix cores.  After the first
+//    half of an odd block every wave is done with that block's super-stage:
+//    wait for the next super-stage's copies, barrier, and refill the free slot
+//    with the super-stage after next (the pipeline of Research results item
+//    1, two stages deep).
+//  * The refill's 16 copies per wave go out one per two MFMAs of the second
+//    half.  Issued in one burst, a wave that alone feeds its SIMD stalls on
+//    the full copy queue: 62.1 against 59.6 us at int8 4096^3 (the 16-wave
+//    kernel: 63.8 us).
+//  * The MFMA is inline assembly with the accumulator tied to its AGPR: with
+//    the builtin the compiler picks the untied form and shuffles all 256
+//    accumulators between register files.  Its operands come straight from
+//    LDS reads (the compiler waits for them); the accumulators are read only
+//    after 32 wait states past the last MFMA.
+__device__ inline uint32_t wide_chunk_of_lane(uint32_t lane) { return (lane & 7u) ^ (lane >> 3); }
+__device__ inline uint32_t wide_frag_offset(uint32_t lane, uint32_t h)
+{
+    const uint32_t r = lane & 15u, c = (lane >> 4) + 4u * h;
+    return (r >> 3) * 1024u + (r & 7u) * 128u + 16u * (c ^ (r & 7u));
+}
+__device__ inline void mfma_tied(i32x4 &c, i32x4 a, i32x4 b)
+{
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_w4_kernel(
+    const int8_t *__restrict__ A, const int8_t *__restrict__ B, void *__restrict__ out,
+    const float *__restrict__ sx, const float *__restrict__ sw,
+    int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n, int32_t ldo, int32_t ksplit)
+{
+    constexpr int FM = 8, FN = 8, SS = 64 * 1024;
+    constexpr int SCALE_BYTES = KIND == KIND_LINEAR ? 2 * 256 * 4 : 0;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * SS + SCALE_BYTES];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wm = wave >> 1, wn = wave & 1u;
+    uint32_t tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, 8u, tm, tn);
+    const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+
+    // Split K as in the other kernels: row blockIdx.y of the grid sums K bytes
+    // [kbeg, kbeg + klen) and adds its partial sums into a zeroed C.
+    const int64_t kbeg = (int64_t)blockIdx.y * ksplit;
+    const int32_t klen = (int32_t)((int64_t)Kb - kbeg < ksplit ? (int64_t)Kb - kbeg : (int64_t)ksplit);
+    const bool accumulate = gridDim.y > 1;
+    const int8_t *Ab = A + m0 * Kb + kbeg;
+    const int8_t *Bb = B + n0 * Kb + kbeg;
+    const int64_t a_bytes = (int64_t)(M - m0) * Kb - kbeg;
+    const int64_t b_bytes = (int64_t)(N - n0) * Kb - kbeg;
+
+    // Copy q (0..7 per operand) of wave w fills half u%2 of block u/2, u = w + 4q.
+    uint32_t voff[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int u = (int)wave + 4 * q;
+        voff[q] = (uint32_t)(((u / 2) * 16 + (u % 2) * 8 + (int)(lane >> 3)) * Kb +
+                             (int)wide_chunk_of_lane(lane) * 16);
+    }
+    const uint32_t smem_base = lds_addr(smem);
+    auto rsrc_a = [&](int ss) {
+        const int64_t k0 = (int64_t)ss * 128;
+        return make_rsrc(Ab + k0, a_bytes > k0 ? (uint64_t)(a_bytes - k0) : 0);
+    };
+    auto rsrc_b = [&](int ss) {
+        const int64_t k0 = (int64_t)ss * 128;
+        return make_rsrc(Bb + k0, b_bytes > k0 ? (uint64_t)(b_bytes - k0) : 0);
+    };
+    auto copy_q = [&](const i32x4 &ra, const i32x4 &rb, uint32_t sbase, int q) {
+        if (q < 8) dma16(ra, voff[q], sbase + ((int)wave + 4 * q) * 1024);
+        else dma16(rb, voff[q - 8], sbase + 32768 + ((int)wave + 4 * (q - 8)) * 1024);
+    };
+    // A pieces past the band's K are zeroed once their super-stage has landed.
+    auto zero_tail = [&](int slot, int64_t k0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int u = (int)wave + 4 * q;
+            if (k0 + (int)wide_chunk_of_lane(lane) * 16 >= klen)
+                *(i32x4 *)(smem + slot * SS + u * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+        }
+    };
+
+    i32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+    const int nss = (klen + 127) / 128;  // super-stages
+    const int nk = (klen + 63) / 64;     // 64-byte blocks
+    const bool k_tail = (klen % 128) != 0;
+    // Linear layer: wave 0 copies sx[m0 .. m0+256) and sw[n0 .. n0+256) into LDS
+    // before the first super-stage (entries past M or N read as zero); the first
+    // stage wait covers these older copies, and the epilogue reads the scales
+    // from LDS (read from global memory at the end of the tile, they made the
+    // layer 5% slower at 8192 x 11008 x 4096).
+    if constexpr (KIND == KIND_LINEAR) {
+        if (wave == 0) {
+            const uint32_t sbase = smem_base + 2 * SS;
+            const i32x4 rx = make_rsrc(sx + m0, (uint64_t)(M - m0) * 4);
+            const i32x4 rw = make_rsrc(sw + n0, (uint64_t)(N - n0) * 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dma4(rx, lane * 4 + q * 256, sbase + q * 256);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dma4(rw, lane * 4 + q * 256, sbase + 1024 + q * 256);
+        }
+    }
+    {
+        const i32x4 ra = rsrc_a(0), rb = rsrc_b(0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) copy_q(ra, rb, smem_base, q);
+    }
+    if (nss > 1) {
+        const i32x4 ra = rsrc_a(1), rb = rsrc_b(1);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) copy_q(ra, rb, smem_base + SS, q);
+        wait_vm_barrier<16>();
+    } else {
+        wait_vm_barrier<0>();
+    }
+    if (k_tail && nss == 1) {
+        zero_tail(0, 0);
+        barrier_lds();
+    }
+    const uint32_t foff0 = wide_frag_offset(lane, 0), foff1 = wide_frag_offset(lane, 1);
+    auto fptr = [&](int t) { return smem + ((t / 2) % 2) * SS + ((t % 2) ? foff1 : foff0); };
+
+    i32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    {
+        const char *f = fptr(0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa0[i] = *(const i32x4 *)(f + (wm * FM + i) * 2048);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb0[j] = *(const i32x4 *)(f + 32768 + (wn * FN + j) * 2048);
+    }
+
+    // Refill state of the current odd block: copies of super-stage cp_ss, if any.
+    i32x4 cra = i32x4{0, 0, 0, 0}, crb = i32x4{0, 0, 0, 0};
+    uint32_t csb = 0;
+    bool cp = false;
+
+    // MFMAs of fragment rows i0 .. i0+3; the second half also reads the next
+    // block's fragments from f and issues the refill copies.
+    auto half = [&](const i32x4 *fa, const i32x4 *fb, int i0, bool second, const char *f,
+                    i32x4 *na, i32x4 *nb) {
+#pragma unroll
+        for (int i = i0; i < i0 + FM / 2; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                mfma_tied(acc[i][j], fb[j], fa[i]);
+                if (second) {
+                    const int q = (i - i0) * 4 + j / 2;  // 0..15
+                    if (j % 2 == 0 && cp) copy_q(cra, crb, csb, q);
+                    if (j % 2 == 1) {
+                        if (q < FM) na[q] = *(const i32x4 *)(f + (wm * FM + q) * 2048);
+                        else nb[q - FM] = *(const i32x4 *)(f + 32768 + (wn * FN + q - FM) * 2048);
+                    }
+                }
+            }
+    };
+    auto body = [&](int t, const i32x4 *ca, const i32x4 *cb, i32x4 *na, i32x4 *nb) {
+        half(ca, cb, 0, false, nullptr, na, nb);
+        if (t % 2 == 1) {
+            wait_vm_barrier<0>();
+            const int ss = t / 2;
+            cp = ss + 2 < nss;
+            if (cp) {
+                cra = rsrc_a(ss + 2);
+                crb = rsrc_b(ss + 2);
+                csb = smem_base + (uint32_t)((ss % 2) * SS);
+            }
+            if (k_tail && ss + 1 == nss - 1) {
+                zero_tail((ss + 1) % 2, (int64_t)(nss - 1) * 128);
+                barrier_lds();
+            }
+        }
+        // After the last block the reads fetch stale LDS that nothing uses.
+        half(ca, cb, FM / 2, true, fptr(t + 1), na, nb);
+        cp = false;
+    };
+    int t = 0;
+    for (; t + 1 < nk; t += 2) {
+        body(t, fa0, fb0, fa1, fb1);
+        body(t + 1, fa1, fb1, fa0, fb0);
+    }
+    if (t < nk) body(t, fa0, fb0, fa1, fb1);
+
+    // The accumulators are read 32 wait states after the last MFMA.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+
+    // Epilogue: lane holds C[m][n..n+3] of each fragment.
+    const bool vec_ok = ((N | ldo) & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + wm * 128 + i * 16 + (lane % 16);
+        if (m >= M) continue;
+        const float *lds_sx = (const float *)(smem + 2 * SS);
+        const float *lds_sw = lds_sx + 256;
+        float scale_m = 0.f;
+        if constexpr (KIND == KIND_LINEAR) scale_m = lds_sx[m - m0];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * 128 + j * 16 + (lane / 16) * 4;
+            if (n >= N) continue;
+            const i32x4 v = acc[i][j];
+            if constexpr (KIND == KIND_LINEAR) {
+                float *o = (float *)out + m * (int64_t)ldo + n;
+                if (vec_ok) {
+                    const f32x4 s = *(const f32x4 *)(lds_sw + (n - n0));
+                    f32x4 r;
+                    r.x = ((float)v.x * scale_m) * s.x;
+                    r.y = ((float)v.y * scale_m) * s.y;
+                    r.z = ((float)v.z * scale_m) * s.z;
+                    r.w = ((float)v.w * scale_m) * s.w;
+                    *(f32x4 *)o = r;
+                } else {
+                    for (int r = 0; r < 4 && n + r < N; ++r) o[r] = ((float)v[r] * scale_m) * lds_sw[n - n0 + r];
+                }
+            } else {
+                int32_t *o = (int32_t *)out + m * (int64_t)ldo + n;
+                if (accumulate) {
+                    for (int r = 0; r < 4 && n + r < N; ++r) atomicAdd(o + r, v[r]);
+                } else if (vec_ok) {
+                    *(i32x4 *)o = v;
+                } else {
+                    for (int r = 0; r < 4 && n + r < N; ++r) o[r] = v[r];
+                }
+            }
+        }
+    }
+}
+
+template <int KIND>
+static hipError_t launch_w4(const void *A, const void *B, void *out, const float *sx, const float *sw,
+                            int64_t M, int64_t N, int64_t Kb, int64_t ldo, int64_t ksplit, hipStream_t s)
+{
+    const uint64_t tm = (uint64_t)((M + 255) / 256), tn = (uint64_t)((N + 255) / 256);
+    if (tm * tn > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    if (ksplit <= 0 || ksplit > Kb) ksplit = Kb;
+    if (ksplit < Kb && (KIND == KIND_LINEAR || ksplit % 128 != 0)) return hipErrorInvalidValue;
+    const uint32_t nsplit = (uint32_t)((Kb + ksplit - 1) / ksplit);
+    hipLaunchKernelGGL((mfma_w4_kernel<KIND>), dim3((uint32_t)(tm * tn), nsplit), dim3(256), 0, s,
+                       (const int8_t *)A, (const int8_t *)B, out, sx, sw, (int32_t)M, (int32_t)N,
+                       (int32_t)Kb, (uint32_t)tm, (uint32_t)tn, (int32_t)ldo, (int32_t)ksplit);
+    return hipGetLastError();
+}
+
 // ---- variant table --------------------------------------------------------
 // index = 3*tile + (stages - 2); tile 0 = small, 1 = medium, 2 = large.
 // Each tile has an LDS budget; the K depth of a stage (BK bytes) is chosen so
@@ -511,7 +779,14 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     }
     constexpr bool b1 = KIND == KIND_B1;
     switch (variant) {
-    case 6: return launch_one<std::conditional_t<b1, L2W8, L2W16>, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+    case 6:
+        // int8 GEMM and linear layer: the four-wave large tile (same 256x256
+        // tile, two stages of 128 K-bytes); int4, 1-bit and the convolution
+        // keep the wave grids below.
+        if constexpr ((KIND == KIND_S8 || KIND == KIND_LINEAR) && !CONV)
+            return launch_w4<KIND>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
+        else
+            return launch_one<std::conditional_t<b1, L2W8, L2W16>, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     case 7: return launch_one<L3W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     case 8:
         return launch_one<std::conditional_t<b1 || KIND == KIND_S4, L4W8, L4W16>, KIND, CONV>(
