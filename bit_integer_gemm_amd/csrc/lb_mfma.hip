@@ -155,7 +155,14 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     // (medium and large tiles; the small tile keeps its five workgroups per CU
     // and reads the scales from global memory).
     constexpr bool LDS_SCALES = KIND == KIND_LINEAR && C::BM >= 128;
-    constexpr bool LATE_COPIES = C::NW == 4 || KIND == KIND_S4;
+    // int4 2-stage large tile: the next stage's copies go out one or a few at
+    // a time between the first K block's MFMAs instead of in one burst after
+    // the barrier.  With 8 waves of 64x128 this ran 2-7% faster than the
+    // 16-wave tile with burst copies on every shape timed (4096^3: 59.9 against
+    // 61.6 us; 8192 x 8192 x 4096: 227.9 against 243.8 us); either change alone
+    // was mixed.
+    constexpr bool SPREAD = KIND == KIND_S4 && C::BM == 256 && C::ST == 2 && !CONV;
+    constexpr bool LATE_COPIES = (C::NW == 4 || KIND == KIND_S4) && !SPREAD;
     constexpr int SCALE_BYTES = LDS_SCALES ? (C::BM + C::BN) * 4 : 0;
     __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE_BYTES + SCALE_BYTES];
 
@@ -261,6 +268,13 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
         }
     };
 
+    // One copy (index i of this wave's NDMA) of a stage into a slot.
+    auto issue_q = [&](const i32x4 &ra, const i32x4 &rb, int slot, int i) {
+        const bool isA = i < C::NDMA_A;
+        const int j = (int)wave + C::NW * (isA ? i : i - C::NDMA_A);
+        dma16(isA ? ra : rb, voff[i], smem_base + slot * C::STAGE_BYTES + (isA ? j : C::ABLK + j) * 1024);
+    };
+
     i32x4 acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -320,7 +334,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
             // 1-bit tiles, 5% slower for the small tile.  The 16-wave int4 tile
             // copies first: holding its fragments over the copies would spill.
             if (kb == 0) {
-                if constexpr (!LATE_COPIES) {
+                if constexpr (!LATE_COPIES && !SPREAD) {
                     if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1, (int)((kt + C::ST - 1) % C::ST));
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -332,8 +346,24 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                     alo[i] = (af[i] << 4) & (int)0xF0F0F0F0;
                     ahi[i] = af[i] & (int)0xF0F0F0F0;
                 }
+                i32x4 sra = i32x4{0, 0, 0, 0}, srb = i32x4{0, 0, 0, 0};
+                const bool scp = SPREAD && kb == 0 && kt + C::ST - 1 < nk;
+                if constexpr (SPREAD) {
+                    if (scp) {
+                        const int64_t k0 = (kt + C::ST - 1) * C::BK;
+                        sra = make_rsrc(Ab + k0, a_bytes > k0 ? (uint64_t)(a_bytes - k0) : 0);
+                        srb = make_rsrc(Bb + k0, b_bytes > k0 ? (uint64_t)(b_bytes - k0) : 0);
+                    }
+                }
 #pragma unroll
                 for (int j = 0; j < C::FN; ++j) {
+                    if constexpr (SPREAD) {
+                        if (scp) {
+#pragma unroll
+                            for (int q = j * C::NDMA / C::FN; q < (j + 1) * C::NDMA / C::FN; ++q)
+                                issue_q(sra, srb, (int)((kt + C::ST - 1) % C::ST), q);
+                        }
+                    }
                     const i32x4 blo = (bf[j] << 4) & (int)0xF0F0F0F0;
                     const i32x4 bhi = bf[j] & (int)0xF0F0F0F0;
 #pragma unroll
@@ -731,7 +761,8 @@ using M4 = MfmaCfg<128, 128, 64, 2, 2, 4>;    // 64 KiB
 // 16 waves win by 4-9% when there are only 16-64 tiles).  The 1-bit kernels
 // use 8 waves throughout: their per-fragment bit work makes the wider wave
 // tile pay at every depth (124 against 137 us at 4096 x 4096 x 8192 bits with
-// the first bit expansion).
+// the first bit expansion).  The int4 GEMM's 2-stage tile uses 8 waves too,
+// with its copies spread between MFMAs (see SPREAD in the kernel).
 using L2W16 = MfmaCfg<256, 256, 128, 4, 4, 2>; // 128 KiB
 using L2W8 = MfmaCfg<256, 256, 128, 4, 2, 2>;  // 128 KiB
 using L3W8 = MfmaCfg<256, 256, 64, 4, 2, 3>;   // 96 KiB
@@ -781,12 +812,13 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     switch (variant) {
     case 6:
         // int8 GEMM and linear layer: the four-wave large tile (same 256x256
-        // tile, two stages of 128 K-bytes); int4, 1-bit and the convolution
-        // keep the wave grids below.
+        // tile, two stages of 128 K-bytes).  int4 GEMM and 1-bit: 8 waves of
+        // 64x128; the convolution: 16 waves of 64x64.
         if constexpr ((KIND == KIND_S8 || KIND == KIND_LINEAR) && !CONV)
             return launch_w4<KIND>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
         else
-            return launch_one<std::conditional_t<b1, L2W8, L2W16>, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+            return launch_one<std::conditional_t<b1 || (KIND == KIND_S4 && !CONV), L2W8, L2W16>, KIND, CONV>(
+                A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     case 7: return launch_one<L3W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     case 8:
         return launch_one<std::conditional_t<b1 || KIND == KIND_S4, L4W8, L4W16>, KIND, CONV>(
