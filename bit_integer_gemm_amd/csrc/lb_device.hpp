@@ -97,7 +97,10 @@ __device__ inline uint32_t lds_addr(const void *p)
 // robin over the 8 XCDs of an MI355X, each with its own L2.  First give each
 // XCD a contiguous run of tile ids, then walk tiles in bands of `group` tile
 // rows so that the tiles an XCD holds at one time share rows of A and columns
-// of B in its L2.
+// of B in its L2.  The band height also sets which rows of A and columns of B
+// all XCDs read at the same time through the shared last-level cache; it was
+// chosen per tile size from measurements (4 for the medium and large tiles, 8
+// for the small one).
 __device__ inline void tile_of_block(uint32_t bid, uint32_t tiles_m, uint32_t tiles_n,
                                      uint32_t group, uint32_t &tm, uint32_t &tn)
 {

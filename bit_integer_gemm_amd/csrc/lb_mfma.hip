@@ -170,8 +170,14 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave / C::WN, wn = wave % C::WN;
 
+    // Bands of 4 tile rows for the medium and large tiles, 8 for the small
+    // one (see tile_of_block).  Measured per variant against 8-row bands, one
+    // build each in one process: the default large tile 4.6-5% faster (int8
+    // 4096^3, 8192 x 8192 x 4096), the 3-stage medium tile 4.5-6.5% (int8 K =
+    // 1024 at 8192^2 and 16384^2), the 1-bit large tile 1.6-4.5%, the 2-stage
+    // medium tile within 0.5%; the small tile 8% slower at 2048^3.
     uint32_t tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, 8u, tm, tn);
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, C::BM >= 128 ? 4u : 8u, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
     // Split K: workgroup row blockIdx.y sums K bytes [kbeg, kbeg + klen) of the
@@ -517,8 +523,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave >> 1, wn = wave & 1u;
+    // Bands of 4 tile rows: against 8, int8 8192 x 8192 x 4096 241.6 against
+    // 283.9 us and 16384 x 4096 x 4096 233.6 against 236.7 us, 4096^3 equal
+    // (bands of 2: 239.6, 267.2, 59.1 us).
     uint32_t tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, 8u, tm, tn);
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4u, tm, tn);
     const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
 
     // Split K as in the other kernels: row blockIdx.y of the grid sums K bytes
