@@ -447,6 +447,28 @@ def test_auto_k_bands_extreme_values():
     assert (got == -56 * K4).all()
 
 
+def test_auto_k_bands_on_the_large_int8_tile():
+    """K bands run through the four-wave large int8 tile (its split-K path:
+    per-band K offsets, A zeroed past the band, atomic adds into a zeroed C)
+    wherever the selection table sends a few-tile int8 product to variant 6.
+    The shapes are found from the table at run time; up to two are compared
+    with the oracle element by element."""
+    found = []
+    for K in (8192, 16384, 32768):
+        for M in (256, 512, 768, 1024, 2048):
+            for N in (256, 512, 768, 1024, 2048):
+                if M * N * K > 1 << 34:
+                    continue
+                if lb.lb_select_variant(lb.LB_S8, M, N, K, 0)[0] == 6 and k_bands("s8", M, N, K) >= 2:
+                    found.append((M, N, K))
+    if not found:
+        pytest.skip("the selection table sends no few-tile int8 product with long K to variant 6")
+    for i, (M, N, K) in enumerate(sorted(found, key=lambda s: s[0] * s[1] * s[2])[:2]):
+        print(f"[parity] k bands on variant 6: s8 {M}x{N}x{K}, {k_bands('s8', M, N, K)} bands", flush=True)
+        A, B = make("s8", M, N, K, 3100 + i)
+        np.testing.assert_array_equal(run("s8", A, B, lb.LB_AUTO), oracle.gemm_s8(A, B))
+
+
 @pytest.mark.parametrize("kind,M,N,K", [("s8", 64, 64, 8192), ("s8", 4000, 4810, 4096)])
 def test_graph_capture_of_automatic_launches(kind, M, N, K):
     """The automatic path's extra launches (the zeroing of C before K bands, or
