@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "lb_internal.hpp"
 
 namespace {
@@ -20,9 +22,21 @@ int check_common(const void *a, const void *b, const void *c, int64_t M, int64_t
     return LB_OK;
 }
 
+// LB_AUTO_VARIANT=v (0..8) in the environment replaces the selector's choice
+// for LB_AUTO; the automatic path's splits still apply.  -1 when unset or not
+// a variant index.
+int auto_override()
+{
+    const char *e = std::getenv("LB_AUTO_VARIANT");
+    if (!e || e[0] < '0' || e[0] > '8' || e[1] != '\0') return -1;
+    return e[0] - '0';
+}
+
 int resolve(int dtype, int variant, int64_t M, int64_t N, int64_t K)
 {
     if (variant != LB_AUTO) return variant;
+    const int forced = auto_override();
+    if (forced >= 0) return forced;
     int best = LB_DEFAULT_VARIANT;
     // cu_count 0: ask the current device; any failure keeps the default.
     if (lb::select_from_table(dtype, M, N, K, 0, &best, nullptr) != LB_OK) return LB_DEFAULT_VARIANT;
@@ -213,7 +227,8 @@ int conv_entry(int kind, int dtype, const void *X, const void *F, int32_t *Y, in
         return LB_ERR_OVERFLOW;
     const int64_t M = N * Ho * Wo, Kb = Kh * Kw * cb;
     int v = variant;
-    if (v == LB_AUTO && lb::select_from_table(dtype, M, Co, K, 0, &v, nullptr) != LB_OK)
+    if (v == LB_AUTO && (v = auto_override()) < 0 &&
+        lb::select_from_table(dtype, M, Co, K, 0, &v, nullptr) != LB_OK)
         v = LB_DEFAULT_VARIANT;
     lb::ConvGeom g;
     g.H = (int32_t)H; g.W = (int32_t)W; g.Cb = (int32_t)cb; g.Kh = (int32_t)Kh; g.Kw = (int32_t)Kw;

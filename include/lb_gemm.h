@@ -44,7 +44,11 @@
  *   when the chosen variant's tiles fill at most a quarter of the CUs and K is
  *   long, LB_AUTO zeroes C with a kernel and cuts K into bands that add their
  *   exact partial sums into C.  Either way the result is the same (integer
- *   sums do not depend on their order); only the launches differ.
+ *   sums do not depend on their order); only the launches differ.  The
+ *   environment variable LB_AUTO_VARIANT, set to one digit 0..8, replaces the
+ *   selector's choice for every LB_AUTO call (GEMMs, linear layer and
+ *   convolutions) and keeps the splits above: for tuning and tests.  Any other
+ *   value is ignored.
  * Errors: every call returns an lb_status and never aborts.  Checks run in this
  *   order, before any HIP call: null pointer, non-positive size, K alignment,
  *   variant range, K limit; then the launch itself (LB_ERR_HIP).

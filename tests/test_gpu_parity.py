@@ -16,6 +16,7 @@ grid runs with the selected variant, compared in full or (large shapes) on
 sampled rows and columns.
 """
 import functools
+import os
 
 import numpy as np
 import pytest
@@ -392,11 +393,13 @@ KB_PER = {"s8": 1, "s4": 2, "b1": 8}   # elements per byte
 ALPHA = {"s8": 2.5, "s4": 2.3, "b1": 1.25}
 
 
-def k_bands(kind, M, N, K):
-    """Number of K bands the library's automatic choice uses for (M, N, K):
-    the cost model of the header's split-K rule, restated."""
+def k_bands(kind, M, N, K, v=None):
+    """Number of K bands the library's automatic choice uses for (M, N, K)
+    (with variant v when LB_AUTO_VARIANT forces it): the cost model of the
+    header's split-K rule, restated."""
     code = {"s8": lb.LB_S8, "s4": lb.LB_S4, "b1": lb.LB_B1}[kind]
-    v = lb.lb_select_variant(code, M, N, K, 0)[0]
+    if v is None:
+        v = lb.lb_select_variant(code, M, N, K, 0)[0]
     info = lb.lb_variant_info(code, v)
     tm, tn = info["tile_m"], info["tile_n"]
     cu = torch.cuda.get_device_properties(0).multi_processor_count
@@ -447,26 +450,46 @@ def test_auto_k_bands_extreme_values():
     assert (got == -56 * K4).all()
 
 
-def test_auto_k_bands_on_the_large_int8_tile():
-    """K bands run through the four-wave large int8 tile (its split-K path:
-    per-band K offsets, A zeroed past the band, atomic adds into a zeroed C)
-    wherever the selection table sends a few-tile int8 product to variant 6.
-    The shapes are found from the table at run time; up to two are compared
-    with the oracle element by element."""
-    found = []
-    for K in (8192, 16384, 32768):
-        for M in (256, 512, 768, 1024, 2048):
-            for N in (256, 512, 768, 1024, 2048):
-                if M * N * K > 1 << 34:
-                    continue
-                if lb.lb_select_variant(lb.LB_S8, M, N, K, 0)[0] == 6 and k_bands("s8", M, N, K) >= 2:
-                    found.append((M, N, K))
-    if not found:
-        pytest.skip("the selection table sends no few-tile int8 product with long K to variant 6")
-    for i, (M, N, K) in enumerate(sorted(found, key=lambda s: s[0] * s[1] * s[2])[:2]):
-        print(f"[parity] k bands on variant 6: s8 {M}x{N}x{K}, {k_bands('s8', M, N, K)} bands", flush=True)
-        A, B = make("s8", M, N, K, 3100 + i)
-        np.testing.assert_array_equal(run("s8", A, B, lb.LB_AUTO), oracle.gemm_s8(A, B))
+@pytest.fixture
+def forced_auto_variant():
+    """Set LB_AUTO_VARIANT for one test and restore the environment after it."""
+    old = os.environ.get("LB_AUTO_VARIANT")
+
+    def force(v):
+        os.environ["LB_AUTO_VARIANT"] = str(v)
+    yield force
+    if old is None:
+        os.environ.pop("LB_AUTO_VARIANT", None)
+    else:
+        os.environ["LB_AUTO_VARIANT"] = old
+
+
+# The selection table sends no few-tile product to the large tiles, so the K
+# bands of the four-wave int8 tile (variant 6) and of the other large tiles are
+# reached by forcing the automatic path's variant.  Ragged M and N, and a band
+# length that leaves a short last band, are among the cases.
+@pytest.mark.parametrize("kind,v,M,N,K", [
+    ("s8", 6, 256, 256, 8192), ("s8", 6, 200, 330, 16384), ("s8", 6, 64, 512, 12288),
+    ("s8", 7, 256, 256, 8192), ("s8", 8, 200, 330, 16384),
+    ("s4", 6, 256, 256, 16384), ("b1", 6, 256, 256, 65536),
+])
+def test_forced_large_tile_k_bands_match_oracle(forced_auto_variant, kind, v, M, N, K):
+    forced_auto_variant(v)
+    bands = k_bands(kind, M, N, K, v)
+    print(f"[parity] forced variant {v} k bands {kind} {M}x{N}x{K}: {bands} bands", flush=True)
+    assert bands >= 2, "shape no longer exercises the K bands"
+    A, B = make(kind, M, N, K, 3100 + v)
+    np.testing.assert_array_equal(run(kind, A, B, lb.LB_AUTO, K), ref(kind, A, B, K))
+
+
+def test_forced_variant_reaches_the_linear_layer(forced_auto_variant):
+    """LB_AUTO_VARIANT also fixes the variant of the linear layer's automatic
+    path (here the four-wave tile on ragged M and N)."""
+    forced_auto_variant(6)
+    M, N, K = 300, 520, 1024
+    X, W = inputs.s8_rows(M, K, 81), inputs.s8_rows(N, K, 82)
+    sx, sw = inputs.scales(M, 83), inputs.scales(N, 84)
+    assert_rel(run_linear(X, W, sx, sw, lb.LB_AUTO), oracle.linear_s8(X, W, sx, sw))
 
 
 @pytest.mark.parametrize("kind,M,N,K", [("s8", 64, 64, 8192), ("s8", 4000, 4810, 4096)])
