@@ -133,6 +133,28 @@ __device__ inline i32x4 mfma16(i32x4 a, i32x4 b, i32x4 c)
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// int4 even-k plane of a packed fragment: (w << 4) & 0xF0F0F0F0 per word.  The
+// shifts go two words at a time as 64-bit shifts; the bits that cross from one
+// word into the next land in a low nibble, which the mask clears.  The unpack
+// is on the int4 loop's critical path (its vector instructions overlap the
+// MFMAs little): two 64-bit shifts instead of four 32-bit ones made every int4
+// variant 1.3-3.4% faster (4096^3, large 2-stage tile: 52.5 against 53.7 us).
+// The compiler turns a 64-bit shift of a 64-bit value into two 32-bit
+// instructions here, hence the one-instruction assembly.
+__device__ inline i32x4 s4_even_plane(i32x4 w)
+{
+    uint64_t p0 = ((uint64_t)(uint32_t)w.y << 32) | (uint32_t)w.x;
+    uint64_t p1 = ((uint64_t)(uint32_t)w.w << 32) | (uint32_t)w.z;
+    asm("v_lshlrev_b64 %0, 4, %1" : "=v"(p0) : "v"(p0));
+    asm("v_lshlrev_b64 %0, 4, %1" : "=v"(p1) : "v"(p1));
+    i32x4 r;
+    r.x = (int32_t)((uint32_t)p0 & 0xF0F0F0F0u);
+    r.y = (int32_t)((uint32_t)(p0 >> 32) & 0xF0F0F0F0u);
+    r.z = (int32_t)((uint32_t)p1 & 0xF0F0F0F0u);
+    r.w = (int32_t)((uint32_t)(p1 >> 32) & 0xF0F0F0F0u);
+    return r;
+}
+
 // Bits of each byte in reverse order, then the whole word shifted down one
 // place: bit s (s < 7) of every byte lands on bit 6 - s of the same byte (bit 7
 // of each byte then holds a bit of the next byte, which no mask below keeps).
@@ -349,7 +371,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                 i32x4 alo[C::FM], ahi[C::FM];
 #pragma unroll
                 for (int i = 0; i < C::FM; ++i) {
-                    alo[i] = (af[i] << 4) & (int)0xF0F0F0F0;
+                    alo[i] = s4_even_plane(af[i]);
                     ahi[i] = af[i] & (int)0xF0F0F0F0;
                 }
                 i32x4 sra = i32x4{0, 0, 0, 0}, srb = i32x4{0, 0, 0, 0};
@@ -370,7 +392,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                                 issue_q(sra, srb, (int)((kt + C::ST - 1) % C::ST), q);
                         }
                     }
-                    const i32x4 blo = (bf[j] << 4) & (int)0xF0F0F0F0;
+                    const i32x4 blo = s4_even_plane(bf[j]);
                     const i32x4 bhi = bf[j] & (int)0xF0F0F0F0;
                     // In the spread-copy tile two waves share each SIMD; the one
                     // entering its MFMA run is issued first, the other's unpack
