@@ -37,7 +37,7 @@
  *   three tile sizes times three pipeline depths, Research results, item 2);
  *   LB_AUTO lets lb_select_variant choose for (dtype, M, N, K).  For the GEMMs
  *   and the linear layer, when that choice is a large-tile variant (one
- *   workgroup per CU) whose last round of tiles would fill less than half the
+ *   workgroup per CU) whose last round of tiles would fill at most half the
  *   CUs, LB_AUTO runs the product as two launches on the stream: the widest
  *   band of leading columns (else rows) of C that fills whole rounds, then the
  *   rest with the variant chosen for its own shape.  For the integer GEMMs,
