@@ -30,12 +30,15 @@ LB_AUTO = -1
 LB_NUM_VARIANTS = 9
 LB_DEFAULT_VARIANT = 7
 K_ALIGN = {LB_S8: 16, LB_S4: 32, LB_B1: 128}
-K_MAX = {LB_S8: 131071, LB_S4: 131071, LB_B1: 33554304}
+K_MAX = {LB_S8: 131071, LB_S4: 131071, LB_B1: 134217600}
+# Longest 1-bit K one kernel pass covers; longer K runs as K bands (see the header).
+B1_PASS_K = 33554304
 CONV_C_ALIGN = {LB_S8: 64, LB_S4: 128}
 
 # Exported symbols of include/lb_gemm.h (checked by the CPU tests).
 EXPORTS = ("lb_gemm_s8", "lb_gemm_s4", "lb_gemm_b1", "lb_gemm_s8_linear", "lb_conv2d_s8",
-           "lb_conv2d_s4", "lb_select_variant", "lb_status_string", "lb_variant_info")
+           "lb_conv2d_s4", "lb_select_variant", "lb_status_string", "lb_variant_info",
+           "lb_build_id")
 
 
 class LbError(RuntimeError):
@@ -48,13 +51,22 @@ _lib = None
 
 
 def load(path: str = LIB_PATH):
-    """Load the library (once).  Raises if it has not been built."""
+    """Load the library (once).  Raises if it has not been built, or if it was
+    built from sources other than the ones in this tree (its lb_build_id()
+    differs from the hash of csrc/ and include/)."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} not found: build it with `python -m bit_integer_gemm_amd._build`")
     lib = ctypes.CDLL(path)
+    lib.lb_build_id.argtypes = []
+    lib.lb_build_id.restype = ctypes.c_char_p
+    from . import _build
+    built, want = lib.lb_build_id().decode(), _build.source_sha()
+    if built != want:
+        raise ImportError(f"{path} was built from sources {built}, the tree holds {want}: "
+                          "rebuild with `python -m bit_integer_gemm_amd._build`")
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     for name in ("lb_gemm_s8", "lb_gemm_s4", "lb_gemm_b1"):
         f = getattr(lib, name)
@@ -79,6 +91,11 @@ def load(path: str = LIB_PATH):
 
 def status_string(status: int) -> str:
     return load().lb_status_string(status).decode()
+
+
+def build_id() -> str:
+    """Source hash stamped into the loaded library."""
+    return load().lb_build_id().decode()
 
 
 # ---------------------------------------------------------------------------

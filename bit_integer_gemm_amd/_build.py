@@ -7,7 +7,9 @@ into one library exporting the C ABI of ``include/lb_gemm.h``.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
+import re
 import subprocess
 import sys
 
@@ -34,9 +36,53 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
+def source_files():
+    """Every file the library is built from: the sources, their headers and
+    generated tables under csrc/, and the public header."""
+    files = [os.path.join(CSRC, f) for f in os.listdir(CSRC)
+             if f.endswith((".hip", ".cpp", ".hpp", ".inc"))]
+    files.append(os.path.join(INCLUDE, "lb_gemm.h"))
+    return sorted(files)
+
+
+def source_sha() -> str:
+    """Hash of the exact text of every source file (16 hex digits).  The build
+    stamps it into the library, which returns it from lb_build_id(), so that a
+    loaded library can be matched with the sources it was built from."""
+    h = hashlib.sha256()
+    for f in source_files():
+        h.update(os.path.relpath(f, ROOT).encode())
+        h.update(b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
+_MARK = re.compile(rb"lb-source-sha:([0-9a-f]{16})")
+
+
+def built_sha(path: str = None):
+    """The source hash stamped into a built library file (read from its bytes,
+    without loading it), or None if there is no library or no stamp."""
+    path = path or LIB
+    if not os.path.exists(path):
+        return None
+    with open(path, "rb") as fh:
+        m = _MARK.search(fh.read())
+    return m.group(1).decode() if m else None
+
+
+def ensure_built(verbose: bool = False) -> str:
+    """Build the library when it is missing or was built from other sources."""
+    if built_sha() != source_sha():
+        build(verbose=verbose)
+    return LIB
+
+
+def _compile(src: str, sha: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, f'-DLB_SOURCE_SHA="{sha}"', "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")
@@ -46,16 +92,19 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sources()
+    sha = source_sha()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda f: _compile(f, sha), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
     os.replace(tmp, LIB)
+    if built_sha() != sha:
+        raise RuntimeError(f"{LIB} does not carry the source hash {sha}")
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} (sources {sha})")
     return LIB
 
 

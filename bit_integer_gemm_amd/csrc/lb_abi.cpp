@@ -8,7 +8,15 @@
 
 #include "lb_internal.hpp"
 
+#ifndef LB_SOURCE_SHA
+#error "LB_SOURCE_SHA (hash of the source files) is set by the build"
+#endif
+
 namespace {
+
+// The build stamps the hash of the source text into the library; the marker
+// also lets a tool read it from the file without loading it.
+const char kBuildMark[] = "lb-source-sha:" LB_SOURCE_SHA;
 
 int check_common(const void *a, const void *b, const void *c, int64_t M, int64_t N, int64_t K,
                  int64_t align, int64_t kmax, int variant)
@@ -133,6 +141,21 @@ int plan_ksplit(int kind, int variant, int64_t M, int64_t N, int64_t kb, int64_t
     return (int)bands;
 }
 
+// 1-bit K limit of one pass.  The 1-bit kernels accumulate 64 per matching
+// bit pair in int32, so one pass covers at most 33,554,304 bits (4,194,288
+// bytes per row).  A longer K runs as bands of whole 128-byte stages, each at
+// most kB1BandBytes, that add their exact counts into C after a zero fill;
+// this applies to every variant, not only to an automatic choice.
+constexpr int64_t kB1PassBytes = 4194288;
+constexpr int64_t kB1BandBytes = 4194176;  // largest multiple of 128 <= kB1PassBytes
+
+int64_t b1_band_bytes(int64_t kb)
+{
+    if (kb <= kB1PassBytes) return kb;
+    const int64_t bands = (kb + kB1BandBytes - 1) / kB1BandBytes;
+    return ((kb + bands - 1) / bands + 127) / 128 * 128;
+}
+
 int run_gemm(int kind, int dtype, int variant, const void *A, const void *B, void *out,
              size_t out_elem, const float *sx, const float *sw, int64_t M, int64_t N, int64_t K,
              int64_t kb, void *stream)
@@ -140,7 +163,19 @@ int run_gemm(int kind, int dtype, int variant, const void *A, const void *B, voi
     Part parts[2] = {{0, M, 0, N, variant}, {0, 0, 0, 0, 0}};
     int np = 1;
     int64_t band = kb;
-    if (variant == LB_AUTO) {
+    if (kind == lb::KIND_B1 && kb > kB1PassBytes) {
+        // Long 1-bit K: bands are required for exactness (see kB1PassBytes).
+        band = b1_band_bytes(kb);
+        if (variant == LB_AUTO) {
+            // An automatic choice may cut K finer still (few tiles, see below).
+            variant = resolve(dtype, LB_AUTO, M, N, K);
+            int64_t finer = kb;
+            if (plan_ksplit(kind, variant, M, N, kb, &finer) > 1 && finer < band) band = finer;
+        }
+        const hipError_t z = lb::launch_zero_i32((int32_t *)out, M * N, (hipStream_t)stream);
+        if (z != hipSuccess) return LB_ERR_HIP;
+        parts[0].variant = variant;
+    } else if (variant == LB_AUTO) {
         const int v = resolve(dtype, LB_AUTO, M, N, K);
         np = plan_parts(dtype, v, M, N, K, parts);
         if (np == 1 && plan_ksplit(kind, v, M, N, kb, &band) > 1) {
@@ -266,6 +301,8 @@ int lb_select_variant(int dtype, int64_t M, int64_t N, int64_t K, int cu_count, 
     if (dtype != LB_S8 && dtype != LB_S4 && dtype != LB_B1) return LB_ERR_VARIANT;
     return lb::select_from_table(dtype, M, N, K, cu_count, best, second);
 }
+
+const char *lb_build_id(void) { return kBuildMark + 14; }
 
 const char *lb_status_string(int status)
 {

@@ -222,8 +222,10 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
         const int j = (int)wave + C::NW * (isA ? i : i - C::NDMA_A);
         const int rows = isA ? C::BM / 16 : C::BN / 16;
         const int rb = j % rows, kb = j / rows;
-        voff[i] = (uint32_t)((rb * 16 + (int)blk_row_of_lane(lane)) * Kb + kb * 64 +
-                             (int)blk_chunk_of_lane(lane) * 16);
+        // 32-bit offsets: at most 255 rows of Kb bytes, below 2^32 for every
+        // accepted K (unsigned arithmetic, so long rows wrap nothing).
+        voff[i] = (uint32_t)(rb * 16 + (int)blk_row_of_lane(lane)) * (uint32_t)Kb +
+                  (uint32_t)(kb * 64 + (int)blk_chunk_of_lane(lane) * 16);
     }
     const uint32_t smem_base = lds_addr(smem);
 
@@ -574,8 +576,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int u = (int)wave + 4 * q;
-        voff[q] = (uint32_t)(((u / 2) * 16 + (u % 2) * 8 + (int)(lane >> 3)) * Kb +
-                             (int)wide_chunk_of_lane(lane) * 16);
+        voff[q] = (uint32_t)((u / 2) * 16 + (u % 2) * 8 + (int)(lane >> 3)) * (uint32_t)Kb +
+                  wide_chunk_of_lane(lane) * 16u;
     }
     const uint32_t smem_base = lds_addr(smem);
     auto rsrc_a = [&](int ss) {

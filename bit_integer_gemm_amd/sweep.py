@@ -290,6 +290,163 @@ def evaluate(table_files, eval_files, eps=EPS, default=DEFAULT):
     }
 
 
+# ---------------------------------------------------------------------------
+# held-out evaluation: off-grid shapes the table and the classifier never saw
+# ---------------------------------------------------------------------------
+
+K_RANGE = {"s8": (256, 16384), "s4": (256, 16384), "b1": (1024, 65536)}
+K_ALIGN = {"s8": 16, "s4": 32, "b1": 128}
+
+
+def heldout_shapes(dtype, n_random=80, seed=20260):
+    """Seeded off-grid shapes for scoring the selection on data it was not
+    built from: `n_random` shapes log-uniform over the sweep's range (M, N in
+    48..16384, K over the dtype's range, K rounded to the alignment rule,
+    powers of two avoided), then shapes that reach the automatic path's
+    two-launch split (a large-tile grid whose last round is at most half
+    full) and its K bands (few tiles, long K)."""
+    import numpy as np
+    g = np.random.Generator(np.random.PCG64(seed + DTYPES[dtype]))
+    lo, hi = K_RANGE[dtype]
+    al = K_ALIGN[dtype]
+
+    def off_pow2(x, step=1):
+        while x & (x - 1) == 0:
+            x += step
+        return x
+    shapes = []
+    while len(shapes) < n_random:
+        M = off_pow2(int(round(2 ** g.uniform(math.log2(48), 14))))
+        N = off_pow2(int(round(2 ** g.uniform(math.log2(48), 14))))
+        K = off_pow2(int(round(2 ** g.uniform(math.log2(lo), math.log2(hi)) / al)) * al, al)
+        if M * N * K > (1 << 40):   # keep every single call under ~0.5 s
+            continue
+        shapes.append((M, N, K))
+    # two-launch split: tiles of 256, T > 256 CUs, last round at most half full
+    for (tm, tn) in [(16, 19), (19, 16), (12, 23), (21, 13), (18, 17), (33, 9)]:
+        K = [1536, 2560, 3584, 4608, 2816, 3328][len(shapes) % 6] * (1 if dtype != "b1" else 4)
+        shapes.append((tm * 256 - 40, tn * 256 - 24, K))
+    # K bands: few tiles, long K
+    for (M, N) in [(96, 80), (200, 150), (300, 260), (130, 520), (520, 130), (60, 1000)]:
+        K = {"s8": 12288, "s4": 16384, "b1": 49152}[dtype] + 3 * al
+        shapes.append((M, N, K))
+    # medium shapes near grid midpoints (sqrt(2) between two measured sizes)
+    for (M, N, K) in [(362, 724, 1448), (1448, 2896, 2896), (5792, 2896, 1456), (2896, 11584, 720),
+                      (724, 5792, 5792), (11584, 1448, 2896), (181, 181, 11584), (2048 + 96, 3072, 2048 + 160)]:
+        K = off_pow2(max(lo, min(hi, K)) // al * al, al)
+        shapes.append((M, N, K))
+    return shapes
+
+
+def run_heldout(dtype, out_path, shapes=None, log=print):
+    """Time the nine variants, twice (in opposite orders, keeping each one's
+    faster median), plus the library's automatic path, on each held-out
+    shape; record what the table and the classifier select.  Also checks that
+    every variant returns the same C as the default."""
+    import torch
+    import bit_integer_gemm_amd as lb
+    lb.load()
+    prewarm(torch)
+    shapes = shapes or heldout_shapes(dtype)
+    done = set()
+    if os.path.exists(out_path):
+        for line in open(out_path):
+            r = json.loads(line)
+            done.add((r["M"], r["N"], r["K"]))
+    call = {"s8": lb.lb_gemm_s8, "s4": lb.lb_gemm_s4, "b1": lb.lb_gemm_b1}[dtype]
+    gen = torch.Generator(device="cuda")
+    f = open(out_path, "a")
+    for i, (M, N, K) in enumerate(shapes):
+        if (M, N, K) in done:
+            continue
+        gen.manual_seed(7_000_000 + 1000 * DTYPES[dtype] + i)
+        if dtype == "s8":
+            A = torch.randint(-128, 128, (M, K), generator=gen, device="cuda", dtype=torch.int8)
+            B = torch.randint(-128, 128, (N, K), generator=gen, device="cuda", dtype=torch.int8)
+        elif dtype == "s4":
+            A = torch.randint(0, 256, (M, K // 2), generator=gen, device="cuda", dtype=torch.uint8)
+            B = torch.randint(0, 256, (N, K // 2), generator=gen, device="cuda", dtype=torch.uint8)
+        else:
+            A = torch.randint(-2 ** 31, 2 ** 31, (M, K // 32), generator=gen, device="cuda", dtype=torch.int32)
+            B = torch.randint(-2 ** 31, 2 ** 31, (N, K // 32), generator=gen, device="cuda", dtype=torch.int32)
+        C = torch.empty(M, N, dtype=torch.int32, device="cuda")
+        call(A, B, C, DEFAULT)
+        ref = C.clone()
+        sel_table = lb.lb_select_variant(DTYPES[dtype], M, N, K, 0)
+        old = os.environ.get("LB_SELECTOR")
+        os.environ["LB_SELECTOR"] = "mlp"
+        sel_mlp = lb.lb_select_variant(DTYPES[dtype], M, N, K, 0)
+        if old is None:
+            os.environ.pop("LB_SELECTOR")
+        else:
+            os.environ["LB_SELECTOR"] = old
+        order = list(range(9)) + ["auto"]
+        best = {}
+        agree = True
+        for rnd in range(2):
+            for v in (order if rnd == 0 else order[::-1]):
+                vv = lb.LB_AUTO if v == "auto" else v
+                t, _ = time_calls(lambda: call(A, B, C, vv), torch)
+                best[v] = min(best.get(v, float("inf")), t)
+                if rnd == 0:
+                    agree = agree and bool(torch.equal(C, ref))
+        rec = {"dtype": dtype, "M": M, "N": N, "K": K, "sec": [best[v] for v in range(9)],
+               "auto_sec": best["auto"], "table": list(sel_table), "mlp": list(sel_mlp),
+               "agree": agree}
+        f.write(json.dumps(rec) + "\n")
+        f.flush()
+        log(f"[heldout] {dtype} {M}x{N}x{K} table v{sel_table[0]} mlp v{sel_mlp[0]} "
+            + " ".join(f"v{v}:{best[v] * 1e6:.1f}" for v in range(9)) + f" auto:{best['auto'] * 1e6:.1f}")
+        if not agree:
+            raise RuntimeError(f"a variant disagrees with the default at {dtype} {M}x{N}x{K}")
+        del A, B, C, ref
+    f.close()
+
+
+def score_heldout(paths, eps=EPS, default=DEFAULT):
+    """Scores of the table and the classifier on held-out timings: violations
+    (selected more than eps slower than the default), top-2 (the fastest is
+    among the two predicted), top-1 within eps, selected / fastest time, and
+    the speedups over the default and over the best single fixed variant
+    (chosen on these shapes, so that comparison favours the fixed variant)."""
+    rows = [json.loads(line) for p in paths for line in open(p)]
+    if not rows:
+        return {}
+
+    def gm(xs):
+        return math.exp(sum(math.log(x) for x in xs) / len(xs))
+    out = {"shapes": len(rows), "eps": eps, "default_variant": default}
+    fixed = min(range(9), key=lambda v: gm([r["sec"][v] / min(r["sec"]) for r in rows]))
+    out["best_fixed_variant"] = fixed
+    for who in ("table", "mlp"):
+        t_sel = [r["sec"][r[who][0]] for r in rows]
+        best = [min(r["sec"]) for r in rows]
+        fastest = [min(range(9), key=lambda v: (r["sec"][v], v)) for r in rows]
+        viol = [(r["M"], r["N"], r["K"], r[who][0], round(r["sec"][r[who][0]] / r["sec"][default], 3))
+                for r in rows if r["sec"][r[who][0]] > (1 + eps) * r["sec"][default]]
+        out[who] = {
+            "violations_slower_than_default": len(viol), "violation_shapes": viol,
+            "top2_accuracy": sum(1 for r, b in zip(rows, fastest) if b in r[who][:2]) / len(rows),
+            "top1_within_eps": sum(1 for ts, b in zip(t_sel, best) if ts <= (1 + eps) * b) / len(rows),
+            "selected_over_fastest_time": {"geomean": gm([ts / b for ts, b in zip(t_sel, best)]),
+                                           "worst": max(ts / b for ts, b in zip(t_sel, best))},
+            "speedup_vs_default": {"geomean": gm([r["sec"][default] / ts for r, ts in zip(rows, t_sel)]),
+                                   "min": min(r["sec"][default] / ts for r, ts in zip(rows, t_sel)),
+                                   "max": max(r["sec"][default] / ts for r, ts in zip(rows, t_sel))},
+            "speedup_vs_best_fixed": {"geomean": gm([r["sec"][fixed] / ts for r, ts in zip(rows, t_sel)]),
+                                      "min": min(r["sec"][fixed] / ts for r, ts in zip(rows, t_sel))},
+        }
+    sp = [r["sec"][default] / r["auto_sec"] for r in rows]
+    sp_sel = [r["sec"][r["table"][0]] / r["auto_sec"] for r in rows]
+    out["automatic_path"] = {
+        "speedup_vs_default": {"geomean": gm(sp), "min": min(sp), "max": max(sp)},
+        "speedup_vs_selected_variant": {"geomean": gm(sp_sel), "min": min(sp_sel), "max": max(sp_sel)},
+        "slower_than_default": [(r["M"], r["N"], r["K"], round(x, 3)) for r, x in zip(rows, sp)
+                                if x < 1 / (1 + eps)]}
+    out["all_variants_agree"] = all(r["agree"] for r in rows)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -306,8 +463,25 @@ def main(argv=None):
     e = sub.add_parser("evaluate")
     e.add_argument("files", nargs="+", help="timing runs made with the compiled table")
     e.add_argument("--json", help="write the report here")
+    h = sub.add_parser("heldout")
+    h.add_argument("--dtype", choices=sorted(DTYPES), default="s8")
+    h.add_argument("--out", required=True)
+    sh = sub.add_parser("score-heldout")
+    sh.add_argument("files", nargs="+")
+    sh.add_argument("--json", help="write the report here")
     a = ap.parse_args(argv)
-    if a.cmd == "run":
+    if a.cmd == "heldout":
+        t0 = time.time()
+        run_heldout(a.dtype, a.out, log=lambda s: print(s, flush=True))
+        print(f"[heldout] done in {time.time() - t0:.1f} s", flush=True)
+    elif a.cmd == "score-heldout":
+        rep = score_heldout(a.files)
+        txt = json.dumps(rep, indent=1)
+        print(txt)
+        if a.json:
+            with open(a.json, "w") as f:
+                f.write(txt + "\n")
+    elif a.cmd == "run":
         t0 = time.time()
         run_sweep(a.dtype, a.out, a.M, a.N, a.K, check=not a.no_check,
                   log=lambda s: print(s, flush=True))

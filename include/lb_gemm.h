@@ -84,15 +84,20 @@ typedef enum { LB_S8 = 0, LB_S4 = 1, LB_B1 = 2 } lb_dtype;
 
 /* K limits: rows must be whole 16-byte chunks, and the worst-case |sum| must
  * fit int32 (16384 * K for int8; the int4 path accumulates 256 * a * b, the
- * same bound).  The 1-bit path accumulates 64 per matching bit pair (each bit
- * position is weighted so that a pair contributes 64 whatever its place in
- * the byte), so 64 * K must fit int32: K < 2^25. */
+ * same bound).  A 1-bit count never exceeds K, but one pass of the 1-bit
+ * kernels accumulates 64 per matching bit pair (each bit position is weighted
+ * so that a pair contributes 64 whatever its place in the byte), so a pass
+ * covers at most 33,554,304 bits.  A longer 1-bit K (any variant) runs as K
+ * bands of at most that many bits: C is zeroed by a fill kernel on the stream
+ * and every band adds its exact counts into C with atomic adds.  The 1-bit
+ * limit itself comes from 32-bit byte offsets inside a 256-row tile of A or
+ * B: 255 rows of K/8 bytes must stay below 2^32, i.e. K < 2^27. */
 #define LB_S8_K_ALIGN 16
 #define LB_S4_K_ALIGN 32
 #define LB_B1_K_ALIGN 128
 #define LB_S8_K_MAX 131071
 #define LB_S4_K_MAX 131071
-#define LB_B1_K_MAX 33554304 /* largest multiple of 128 below 2^25 */
+#define LB_B1_K_MAX 134217600 /* largest multiple of 128 below 2^27 */
 
 /*
  * C = A x B, int8 operands, int32 result.
@@ -181,6 +186,11 @@ int lb_conv2d_s4(const uint8_t *X, const uint8_t *F, int32_t *Y, int64_t N,
  */
 int lb_select_variant(int dtype, int64_t M, int64_t N, int64_t K, int cu_count,
                       int *best, int *second);
+
+/* Hash of the source files this library was built from (16 hex digits, static
+ * storage; never NULL).  The build stamps it in, so that a caller can check a
+ * loaded library against the sources it expects. */
+const char *lb_build_id(void);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *lb_status_string(int status);

@@ -15,9 +15,8 @@ HEADER = os.path.join(ROOT, "include", "lb_gemm.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(lb.LIB_PATH):
-        from bit_integer_gemm_amd import _build
-        _build.build()
+    from bit_integer_gemm_amd import _build
+    _build.ensure_built()
     return lb.load()
 
 
@@ -32,6 +31,13 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(lb.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_library_carries_the_source_hash(lib):
+    """The loaded library was built from the sources in this tree."""
+    from bit_integer_gemm_amd import _build
+    assert _build.built_sha() == _build.source_sha() == lb.build_id()
+    assert len(lb.build_id()) == 16
 
 
 def test_header_constants_match_binding():
@@ -55,7 +61,7 @@ NULL = ctypes.c_void_p(0)
 
 
 @pytest.mark.parametrize("fn,align,kmax", [("lb_gemm_s8", 16, 131071), ("lb_gemm_s4", 32, 131071),
-                                           ("lb_gemm_b1", 128, 33554304)])
+                                           ("lb_gemm_b1", 128, 134217600)])
 def test_gemm_argument_checks(lib, fn, align, kmax):
     f = getattr(lib, fn)
     assert f(NULL, FAKE, FAKE, 4, 4, align, -1, NULL) == lb.LB_ERR_NULL

@@ -11,9 +11,10 @@ back untouched.  Small shapes cover ragged M, N (not multiples of any tile), K
 shorter than one pipeline stage, K not a multiple of the stage, and single rows
 and columns.  The full-size workloads run in the launch configuration the
 benchmark times (automatic variant choice) and are checked element by element
-against the oracle, plus a Freivalds product check; the variant sweep's shape
-grid runs with the selected variant, compared in full or (large shapes) on
-sampled rows and columns.
+against the oracle, plus a Freivalds product check.  The variant sweep's whole
+shape grid (324 shapes per bit width) runs with the automatic choice: compared
+with the oracle in full up to 2^30 multiply-adds, and above that on sampled
+whole rows and columns plus a Freivalds check of all of C on the device.
 """
 import functools
 import os
@@ -110,12 +111,15 @@ def test_auto_and_variants_mid_size_s8(variant):
 
 
 def test_extreme_values_at_max_k():
-    """Largest-magnitude operands at the largest K the boundary accepts."""
+    """Largest-magnitude operands at the largest K the boundary accepts, on the
+    three int8 kernels the variants use (variant 6 is the four-wave tile whose
+    MFMAs are inline assembly on tied accumulators) and the int4 kernels: all
+    -128 gives 16384*K, and for int4 all -8 gives the largest sum, 64*K."""
     M, N = 33, 47
     K = 131056  # largest multiple of 16 <= 131071
     A = np.full((M, K), -128, np.int8)
     B = np.full((N, K), -128, np.int8)
-    for v in (7, 2, 5):
+    for v in (6, 7, 2, 5):
         print(f"[parity] s8 extreme v{v}", flush=True)
         got = run("s8", A, B, v)
         assert (got == 16384 * K).all()
@@ -125,6 +129,11 @@ def test_extreme_values_at_max_k():
     for v in (7, 2):
         got = run("s4", A4, B4, v)
         assert (got == -56 * K4).all()
+    B4m = inputs.pack_s4(np.full((N, K4), -8, np.int8))
+    for v in (6, 7, 2):
+        print(f"[parity] s4 extreme all -8 v{v}", flush=True)
+        got = run("s4", A4, B4m, v)
+        assert (got == 64 * K4).all()
     Kb = 8192
     ones = np.full((M, Kb // 32), 0xFFFFFFFF, np.uint32)
     for v in (7, 0):
@@ -134,27 +143,60 @@ def test_extreme_values_at_max_k():
         assert (run("b1", fives, aas, v) == 0).all()
 
 
-B1_MAX_K_CASE = (17, 9, lb.K_MAX[lb.LB_B1])
+B1_PASS_K_CASE = (17, 9, lb.B1_PASS_K)
 
 
 @functools.lru_cache(maxsize=1)
-def b1_max_k_case():
-    M, N, K = B1_MAX_K_CASE
+def b1_pass_k_case():
+    M, N, K = B1_PASS_K_CASE
     A, B = inputs.b1_rows(M, K, 31), inputs.b1_rows(N, K, 32)
     return A, B, oracle.gemm_b1(A, B, K)
 
 
 @pytest.mark.parametrize("variant", list(range(9)))
-def test_b1_at_max_k(variant):
-    """The largest 1-bit K the boundary accepts, where the kernel's accumulator
-    (64 per matching bit pair) comes within 8192 of the int32 limit: all ones
-    give K exactly, and random bits match the oracle."""
-    M, N, K = B1_MAX_K_CASE
+def test_b1_at_longest_single_pass_k(variant):
+    """The longest 1-bit K one kernel pass covers, where the kernel's
+    accumulator (64 per matching bit pair) comes within 8192 of the int32
+    limit: all ones give K exactly, and random bits match the oracle."""
+    M, N, K = B1_PASS_K_CASE
     print(f"[parity] b1 K={K} v{variant}", flush=True)
     ones = np.full((M, K // 32), 0xFFFFFFFF, np.uint32)
     assert (run("b1", ones, ones[:N], variant) == K).all()
-    A, B, want = b1_max_k_case()
+    A, B, want = b1_pass_k_case()
     np.testing.assert_array_equal(run("b1", A, B, variant), want)
+
+
+B1_LONG_K_CASE = (17, 9, (1 << 26) + 384)   # three K bands
+
+
+@functools.lru_cache(maxsize=1)
+def b1_long_k_case():
+    M, N, K = B1_LONG_K_CASE
+    A, B = inputs.b1_rows(M, K, 33), inputs.b1_rows(N, K, 34)
+    return A, B, oracle.gemm_b1(A, B, K)
+
+
+@pytest.mark.parametrize("variant", [lb.LB_AUTO] + list(range(9)))
+def test_b1_long_k_runs_as_bands(variant):
+    """1-bit K beyond one pass (here 2^26 + 384 bits, three bands), for every
+    variant and the automatic choice: the bands' counts add up exactly."""
+    M, N, K = B1_LONG_K_CASE
+    print(f"[parity] b1 long K={K} v{variant}", flush=True)
+    A, B, want = b1_long_k_case()
+    np.testing.assert_array_equal(run("b1", A, B, variant), want)
+
+
+@pytest.mark.parametrize("variant", [lb.LB_AUTO, 0, 6, 7])
+def test_b1_at_max_k(variant):
+    """The largest 1-bit K the boundary accepts (2^27 - 128 bits, four bands):
+    all ones give K, and complementary bit patterns give 0 and K/2."""
+    M, N, K = 17, 9, lb.K_MAX[lb.LB_B1]
+    print(f"[parity] b1 K={K} v{variant}", flush=True)
+    ones = np.full((M, K // 32), 0xFFFFFFFF, np.uint32)
+    assert (run("b1", ones, ones[:N], variant) == K).all()
+    fives = np.full((M, K // 32), 0x55555555, np.uint32)
+    assert (run("b1", fives, np.full((N, K // 32), 0xAAAAAAAA, np.uint32), variant) == 0).all()
+    assert (run("b1", fives, fives[:N], variant) == K // 2).all()
 
 
 def test_b1_equals_int8_gemm_of_unpacked_bits():
@@ -171,6 +213,12 @@ def test_b1_equals_int8_gemm_of_unpacked_bits():
         torch.cuda.synchronize()
         for v in [lb.LB_AUTO] + list(range(lb.LB_NUM_VARIANTS)):
             np.testing.assert_array_equal(run("b1", A1, B1, v), C8.cpu().numpy(), err_msg=f"{M}x{N}x{K} v{v}")
+
+
+def test_loaded_library_matches_sources():
+    """The library the GPU tests run was built from this tree's sources."""
+    from bit_integer_gemm_amd import _build
+    assert lb.build_id() == _build.source_sha()
 
 
 def test_transpose_identity_on_gpu():
@@ -234,21 +282,75 @@ def test_full_size_exact(kind, M, N, K, seeds):
 
 
 # The shape grid of the variant sweep (M, N over 64 .. 16384, four K per bit
-# width), on the sweep's own operands, with the variant the library selects for
-# each shape.  Shapes up to 2^22 outputs are covered (240 per bit width); the
-# larger ones run the same kernels and are covered by the full-size workloads
-# above and by the sweep's check that all nine variants agree.
+# width: all 324 shapes per bit width), on the sweep's own operands, with the
+# library's automatic choice.  Shapes up to 2^30 multiply-adds are compared
+# with the oracle element by element.  Larger ones (up to 16384^2 x 8192, and
+# 1-bit K up to 32768) are compared with the oracle on sampled whole rows and
+# columns (the first and last of each, plus random ones), and all of C is
+# checked by Freivalds' test on the device: C x == A (B^T x) for random integer
+# vectors x, in fp64, where every product and partial sum is an integer below
+# 2^53 and therefore exact in any summation order (|C x| and |A (B^T x)| are
+# at most 128 * 64 * 16384 * 128 * 8192 < 2^48 here).
 GRID_MN = [2 ** e for e in range(6, 15)]
 GRID_K = {"s8": [256, 1024, 4096, 8192], "s4": [256, 1024, 4096, 8192], "b1": [1024, 4096, 8192, 32768]}
 DTYPE_CODE = {"s8": 0, "s4": 1, "b1": 2}
+FULL_COMPARE_MACS = 1 << 30
 
 
+def decode_dev(kind, X, r0, r1):
+    """Rows r0..r1 of a device operand as fp64 values (int8 bytes, signed
+    nibbles with the even k in the low nibble, or bits with k in bit k % 32)."""
+    x = X[r0:r1]
+    if kind == "s8":
+        return x.to(torch.float64)
+    if kind == "s4":
+        p = x.to(torch.int32)
+        lo = ((p & 15) ^ 8) - 8
+        hi = (((p >> 4) & 15) ^ 8) - 8
+        return torch.stack((lo, hi), dim=2).reshape(x.shape[0], -1).to(torch.float64)
+    shifts = torch.arange(32, device=x.device, dtype=torch.int32)
+    bits = (x.unsqueeze(-1) >> shifts) & 1
+    return bits.reshape(x.shape[0], -1).to(torch.float64)
+
+
+def freivalds_dev(kind, dA, dB, C, seed, reps=2, chunk=2048):
+    """C x == A (B^T x) on the device, exactly (see above), for `reps` random
+    vectors x with entries in [-64, 64]."""
+    M, N = C.shape
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    for _ in range(reps):
+        x = torch.randint(-64, 65, (N,), generator=g, device="cuda").to(torch.float64)
+        v = None
+        for r in range(0, N, chunk):
+            part = decode_dev(kind, dB, r, min(N, r + chunk)).T @ x[r:r + chunk]
+            v = part if v is None else v + part
+        for r in range(0, M, chunk):
+            lhs = C[r:r + chunk].to(torch.float64) @ x
+            rhs = decode_dev(kind, dA, r, min(M, r + chunk)) @ v
+            bad = (lhs != rhs).nonzero()
+            assert bad.numel() == 0, f"Freivalds check fails on {bad.numel()} rows from row {r}"
+
+
+def sampled_check_dev(kind, A, B, K, C, rng, nrows=3, ncols=3):
+    """Whole rows and columns of a device C against the oracle (sliced on the
+    device, so only the sampled outputs are copied back)."""
+    M, N = C.shape
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, nrows, replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, ncols, replace=False)]))
+    got_r = C[torch.from_numpy(rows).cuda()].cpu().numpy()
+    got_c = C[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    np.testing.assert_array_equal(got_r, ref(kind, np.ascontiguousarray(A[rows]), B, K))
+    np.testing.assert_array_equal(got_c, ref(kind, A, np.ascontiguousarray(B[cols]), K))
+
+
+@pytest.mark.parametrize("kidx", range(4))
 @pytest.mark.parametrize("kind", ["s8", "s4", "b1"])
-def test_sweep_grid_selected_variant(kind):
-    shapes = [(M, N) for M in GRID_MN for N in GRID_MN if M * N <= 1 << 22]
-    Mmax, Nmax = max(M for M, _ in shapes), max(N for _, N in shapes)
-    g = inputs.rng(777)
-    for kidx, K in enumerate(GRID_K[kind]):
+def test_sweep_grid_selected_variant(kind, kidx):
+    shapes = [(M, N) for M in GRID_MN for N in GRID_MN]
+    Mmax, Nmax = max(GRID_MN), max(GRID_MN)
+    g = inputs.rng(777 + kidx)
+    for K in GRID_K[kind][kidx:kidx + 1]:
         sa = 4_000_000 + 100 * DTYPE_CODE[kind] + kidx
         sb = 4_500_000 + 100 * DTYPE_CODE[kind] + kidx
         rows = {"s8": inputs.s8_rows, "s4": inputs.s4_rows, "b1": inputs.b1_rows}[kind]
@@ -257,18 +359,40 @@ def test_sweep_grid_selected_variant(kind):
         if kind == "b1":
             dA, dB = dA.view(torch.int32), dB.view(torch.int32)
         call = {"s8": lb.lb_gemm_s8, "s4": lb.lb_gemm_s4, "b1": lb.lb_gemm_b1}[kind]
-        print(f"[parity] grid {kind} K={K}: {len(shapes)} shapes", flush=True)
+        n_full = sum(1 for M, N in shapes if M * N * K <= FULL_COMPARE_MACS)
+        print(f"[parity] grid {kind} K={K}: {len(shapes)} shapes, {n_full} compared in full, "
+              f"{len(shapes) - n_full} sampled + Freivalds", flush=True)
         for M, N in shapes:
             C = torch.empty(M, N, dtype=torch.int32, device="cuda")
             call(dA[:M], dB[:N], C, lb.LB_AUTO)
             torch.cuda.synchronize()
-            Ch = C.cpu().numpy()
-            if M * N * K <= 1 << 30:
-                np.testing.assert_array_equal(Ch, ref(kind, A[:M], B[:N], K), err_msg=f"{M}x{N}x{K}")
+            if M * N * K <= FULL_COMPARE_MACS:
+                np.testing.assert_array_equal(C.cpu().numpy(), ref(kind, A[:M], B[:N], K),
+                                              err_msg=f"{M}x{N}x{K}")
             else:
-                sampled_check(kind, A[:M], B[:N], K, Ch, g, nrows=3, ncols=3)
+                sampled_check_dev(kind, A[:M], B[:N], K, C, g)
+                freivalds_dev(kind, dA[:M], dB[:N], C, seed=M * 131 + N * 7 + K)
+            del C
         del dA, dB
         torch.cuda.empty_cache()
+
+
+def test_freivalds_dev_detects_a_wrong_element():
+    """The device Freivalds check fails when one element of C is off by one."""
+    M, N, K = 300, 260, 512
+    A, B = make("s8", M, N, K, 4711)
+    dA, dB = to_dev(A), to_dev(B)
+    C = to_dev(oracle.gemm_s8(A, B))
+    freivalds_dev("s8", dA, dB, C, seed=1)
+    for kind in ("s4", "b1"):
+        A2, B2 = make(kind, M, N, 1024, 4712)
+        d2A, d2B = to_dev(A2), to_dev(B2)
+        if kind == "b1":
+            d2A, d2B = d2A.view(torch.int32), d2B.view(torch.int32)
+        freivalds_dev(kind, d2A, d2B, to_dev(ref(kind, A2, B2, 1024)), seed=2)
+    C[123, 45] += 1
+    with pytest.raises(AssertionError):
+        freivalds_dev("s8", dA, dB, C, seed=1)
 
 
 # ---------------------------------------------------------------------------

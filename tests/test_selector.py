@@ -29,9 +29,8 @@ def table_entries():
 
 @pytest.fixture(scope="module", autouse=True)
 def lib():
-    if not os.path.exists(lb.LIB_PATH):
-        from bit_integer_gemm_amd import _build
-        _build.build()
+    from bit_integer_gemm_amd import _build
+    _build.ensure_built()
     lb.load()
     old = os.environ.pop("LB_SELECTOR", None)
     yield
