@@ -32,11 +32,20 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# MI355X spec-sheet peaks (dense, no sparsity).  The 1-bit GEMM expands bits
-# to int8 bytes and runs on the int8 MFMA, one int8 MAC per bit-MAC, so it is
-# measured against the same 5033.2 TOP/s.
+# MI355X spec-sheet peaks (dense, no sparsity).  int8 MFMA: 256 CUs x 4 SIMDs
+# x 32768 ops per 16-cycle v_mfma_i32_16x16x64_i8 x 2.4 GHz.  The 1-bit GEMM
+# feeds bit planes to the FP4 MFMA, one e2m1 MAC per bit-MAC, so it is measured
+# against the FP4 peak: 65536 ops per 16-cycle 16x16x128 instruction, 10.07
+# P op/s (spec sheet: 10.1 PFLOP/s dense fp4).  int4 has no MFMA of its own
+# and counts against the int8 peak.
 PEAK_INT8_TOPS = 256 * 2.4e9 * 8192 / 1e12          # 5033.2 TOP/s, int8 MFMA
+PEAK_FP4_TOPS = 256 * 2.4e9 * 16384 / 1e12          # 10066.3 TOP/s, FP4 MFMA
 PEAK_HBM_GBS = 8000.0
+
+
+def peak_tops(dtype):
+    return PEAK_FP4_TOPS if dtype == "b1" else PEAK_INT8_TOPS
+
 
 WORKLOADS = {
     # name: (dtype, M, N, K, seeds)
@@ -266,8 +275,17 @@ def measure(workload, torch, lb):
         t_sel = min(t_sel, time_calls(lambda: run(sel), torch, target_ms=30.0, groups=5)[0])
         t_def = min(t_def, time_calls(lambda: run(lb.LB_DEFAULT_VARIANT), torch, target_ms=30.0, groups=5)[0])
     t_cold = time_cold(lambda: run(), torch)
+    t_int8_route = None
+    if dtype == "b1":
+        # the 1-bit GEMM's int8 route (weighted bit planes on the int8 MFMA)
+        # beside the FP4 route that the library uses: the A/B of that choice
+        os.environ["LB_B1_ROUTE"] = "int8"
+        try:
+            t_int8_route = min(time_calls(lambda: run(), torch, target_ms=30.0, groups=5)[0] for _ in range(2))
+        finally:
+            del os.environ["LB_B1_ROUTE"]
     ops = 2.0 * M * N * K
-    peak = PEAK_INT8_TOPS
+    peak = peak_tops(dtype)
     tops = ops / t_auto / 1e12
     res = {"tops": round(tops, 2), "frac_of_peak": round(tops / peak, 4), "peak_tops": round(peak, 1),
            "us_per_call": round(t_auto * 1e6, 2), "variant": sel,
@@ -277,6 +295,10 @@ def measure(workload, torch, lb):
            "cold_us_per_call": round(t_cold * 1e6, 2), "cold_tops": round(ops / t_cold / 1e12, 2)}
     if dtype != "b1":
         res.update(vendor_int8(M, N, K, torch, t_sel))
+    else:
+        res.update({"int8_route_us": round(t_int8_route * 1e6, 2),
+                    "fp4_route_speedup_vs_int8_route": round(t_int8_route / t_auto, 4),
+                    "int8_route_frac_of_int8_peak": round(ops / t_int8_route / 1e12 / PEAK_INT8_TOPS, 4)})
     return res
 
 
@@ -388,7 +410,7 @@ def main():
     ms_per_step = t / args.steps * 1e3
     ops = 2.0 * M * N * K
     value = ops * args.steps / t / 1e12
-    peak = PEAK_INT8_TOPS
+    peak = peak_tops(dtype)
     sha = kernel_source_sha()
     traffic, traffic_note = load_traffic(args.workload, sha)
 
@@ -404,7 +426,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"s4": "int4 (int8 MFMA, int32 acc)", "s8": "int8 (int32 acc)",
-                  "b1": "1-bit (bits expanded to int8 on MFMA, int32 acc)",
+                  "b1": "1-bit (bit planes on the FP4 MFMA, exact fp32 acc)",
                   "linear": "int8 (int32 acc) + fp32 dequant"}[dtype],
         "data": "synthetic (seeded uniform operands, resident in HBM)",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "variant": variant,

@@ -31,8 +31,10 @@ LB_NUM_VARIANTS = 9
 LB_DEFAULT_VARIANT = 7
 K_ALIGN = {LB_S8: 16, LB_S4: 32, LB_B1: 128}
 K_MAX = {LB_S8: 131071, LB_S4: 131071, LB_B1: 134217600}
-# Longest 1-bit K one kernel pass covers; longer K runs as K bands (see the header).
-B1_PASS_K = 33554304
+# Longest 1-bit K one kernel pass covers, per matrix-instruction route (FP4, the
+# default, sums in fp32, exact to 2^24; the int8 route, LB_B1_ROUTE=int8, sums 64
+# per pair in int32); longer K runs as K bands (see the header).
+B1_PASS_K = {"fp4": 1 << 24, "int8": 33554304}
 CONV_C_ALIGN = {LB_S8: 64, LB_S4: 128}
 
 # Exported symbols of include/lb_gemm.h (checked by the CPU tests).

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
+#include <cstring>
 
 #include "lb_internal.hpp"
 
@@ -104,8 +105,9 @@ int plan_parts(int dtype, int variant, int64_t M, int64_t N, int64_t K, Part *pa
 // with atomic adds; integer addition makes the result independent of their
 // order.  S comes from a cost model fitted to measurements on MI355X: a
 // one-round product takes about alpha ns per element of K (2.5 int8, 2.3 int4,
-// 1.25 1-bit); S bands take alpha K / S, plus ~3 us for the zeroing launch,
-// plus ~15 ps per atomic add (M N S of them).  The S (2..16, at most
+// 0.83 1-bit on the FP4 route, 1.25 on the int8 route); S bands take
+// alpha K / S, plus ~3 us for the zeroing launch, plus ~15 ps per atomic add
+// (M N S of them).  The S (2..16, at most
 // CUs / tiles and whole 128-byte stages) with the lowest estimate is used when
 // that estimate beats alpha K by 1.3x (measured: int8 64 x 64 x 8192 2.9x
 // faster, 1-bit 64 x 64 x 32768 4.9x; the model declines 64 x 4096 x 4096 and
@@ -121,7 +123,10 @@ int plan_ksplit(int kind, int variant, int64_t M, int64_t N, int64_t kb, int64_t
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     if (4 * tiles > cu) return 1;
     const int per_byte = kind == lb::KIND_S8 ? 1 : kind == lb::KIND_S4 ? 2 : 8;
-    const double alpha = kind == lb::KIND_S8 ? 2.5 : kind == lb::KIND_S4 ? 2.3 : 1.25;
+    const double alpha = kind == lb::KIND_S8    ? 2.5
+                         : kind == lb::KIND_S4  ? 2.3
+                         : kind == lb::KIND_B1F4 ? 0.83
+                                                 : 1.25;
     const double t0 = alpha * (double)kb * per_byte;
     const int64_t step = 128;  // a multiple of every variant's stage depth
     int64_t smax = cu / tiles;
@@ -141,18 +146,33 @@ int plan_ksplit(int kind, int variant, int64_t M, int64_t N, int64_t kb, int64_t
     return (int)bands;
 }
 
-// 1-bit K limit of one pass.  The 1-bit kernels accumulate 64 per matching
-// bit pair in int32, so one pass covers at most 33,554,304 bits (4,194,288
-// bytes per row).  A longer K runs as bands of whole 128-byte stages, each at
-// most kB1BandBytes, that add their exact counts into C after a zero fill;
-// this applies to every variant, not only to an automatic choice.
-constexpr int64_t kB1PassBytes = 4194288;
-constexpr int64_t kB1BandBytes = 4194176;  // largest multiple of 128 <= kB1PassBytes
-
-int64_t b1_band_bytes(int64_t kb)
+// The 1-bit GEMM's matrix instruction: FP4 (four bit planes per 64-byte
+// block, fp32 sums; one instruction covers 128 K bits) by default, or int8
+// (eight weighted planes, int32 sums; 64 K bits per instruction).  Measured
+// on MI355X, every variant, bit-identical results: FP4 1.27-1.59x faster
+// (4096 x 4096 x 8192 bits 51.0 against 79.8 us, 8192^3 198.9 against 312.6
+// us).  LB_B1_ROUTE=int8 in the environment selects the int8 route (for A/B
+// measurement and its parity tests).
+int b1_kind()
 {
-    if (kb <= kB1PassBytes) return kb;
-    const int64_t bands = (kb + kB1BandBytes - 1) / kB1BandBytes;
+    const char *e = std::getenv("LB_B1_ROUTE");
+    if (e && std::strcmp(e, "int8") == 0) return lb::KIND_B1;
+    return lb::KIND_B1F4;
+}
+
+// 1-bit K limit of one pass.  The int8 route accumulates 64 per matching bit
+// pair in int32, so one pass covers at most 33,554,304 bits (4,194,288 bytes
+// per row); the FP4 route accumulates 1.0 per pair in fp32, exact up to 2^24
+// (2,097,152 bytes).  A longer K runs as bands of whole 128-byte stages, each
+// within the pass limit, that add their exact counts into C after a zero fill;
+// this applies to every variant, not only to an automatic choice.
+int64_t b1_pass_bytes(int kind) { return kind == lb::KIND_B1F4 ? 2097152 : 4194288; }
+
+int64_t b1_band_bytes(int kind, int64_t kb)
+{
+    const int64_t pass = b1_pass_bytes(kind), bmax = pass / 128 * 128;
+    if (kb <= pass) return kb;
+    const int64_t bands = (kb + bmax - 1) / bmax;
     return ((kb + bands - 1) / bands + 127) / 128 * 128;
 }
 
@@ -163,9 +183,10 @@ int run_gemm(int kind, int dtype, int variant, const void *A, const void *B, voi
     Part parts[2] = {{0, M, 0, N, variant}, {0, 0, 0, 0, 0}};
     int np = 1;
     int64_t band = kb;
-    if (kind == lb::KIND_B1 && kb > kB1PassBytes) {
-        // Long 1-bit K: bands are required for exactness (see kB1PassBytes).
-        band = b1_band_bytes(kb);
+    const bool b1 = kind == lb::KIND_B1 || kind == lb::KIND_B1F4;
+    if (b1 && kb > b1_pass_bytes(kind)) {
+        // Long 1-bit K: bands are required for exactness (see b1_pass_bytes).
+        band = b1_band_bytes(kind, kb);
         if (variant == LB_AUTO) {
             // An automatic choice may cut K finer still (few tiles, see below).
             variant = resolve(dtype, LB_AUTO, M, N, K);
@@ -219,7 +240,7 @@ int lb_gemm_b1(const uint32_t *A, const uint32_t *B, int32_t *C, int64_t M, int6
 {
     int st = check_common(A, B, C, M, N, K, LB_B1_K_ALIGN, LB_B1_K_MAX, variant);
     if (st != LB_OK) return st;
-    return run_gemm(lb::KIND_B1, LB_B1, variant, A, B, C, 4, nullptr, nullptr, M, N, K, K / 8, stream);
+    return run_gemm(b1_kind(), LB_B1, variant, A, B, C, 4, nullptr, nullptr, M, N, K, K / 8, stream);
 }
 
 int lb_gemm_s8_linear(const int8_t *X, const int8_t *W, const float *sx, const float *sw,

@@ -6,7 +6,10 @@
 
 namespace lb {
 
-enum { KIND_S8 = 0, KIND_S4 = 1, KIND_LINEAR = 2, KIND_B1 = 3 };
+// KIND_B1 runs the 1-bit GEMM on the int8 instruction (eight weighted bit
+// planes per 64-byte block), KIND_B1F4 on the FP4 instruction (four bit planes
+// per block, fp32 accumulation exact below 2^24).
+enum { KIND_S8 = 0, KIND_S4 = 1, KIND_LINEAR = 2, KIND_B1 = 3, KIND_B1F4 = 4 };
 
 // int8 MFMA family (int8 GEMM, packed-int4 GEMM, int8 linear layer, and the
 // 1-bit GEMM on weighted bit planes).  Kb is the row length of A and B in

@@ -166,6 +166,33 @@ __device__ inline i32x4 mirror_bytes_shr1(i32x4 w)
     return (i32x4)u;
 }
 
+// 1-bit route on the FP4 matrix instruction (v_mfma_scale_f32_16x16x128_f8f6f4
+// with e2m1 operands on both sides).  Plane s (0..3) of a lane's 16 bytes keeps
+// bit 4j+s of every word in nibble j, the rest of the nibble zero: 32 e2m1
+// values per lane, each 0 or 2^(s-1) (nibble codes 0001 = 0.5, 0010 = 1.0,
+// 0100 = 2.0).  Bit 3 of a nibble is the e2m1 sign bit (0.0 or -0.0 alone), so
+// plane 3 is shifted down one place and takes the code 0100 = 2.0.  A and B
+// get the same planes, so the product of two set bits is 4^(s-1) (planes 0-2)
+// or 4 (plane 3), and the E8M0 block scales 2^(1-s) (2^-1 for plane 3) on each
+// operand bring every such product to exactly 1.0.  The fp32 accumulator then
+// holds the count exactly while it stays below 2^24.  One instruction covers
+// 128 K bits of a 16x16 tile, twice the int8 route's 64.
+template <int S>
+__device__ inline i32x4 fp4_plane(i32x4 w)
+{
+    const u32x4 u = (u32x4)w;
+    if constexpr (S < 3) return (i32x4)(u & (0x11111111u << S));
+    else return (i32x4)((u >> 1) & 0x44444444u);
+}
+template <int S>
+__device__ inline f32x4 mfma_fp4(i32x4 b, i32x4 a, f32x4 c)
+{
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    constexpr int sc = S == 0 ? 128 : S == 1 ? 127 : 126;  // E8M0: 2^(sc - 127)
+    const i32x8 b8 = {b.x, b.y, b.z, b.w, 0, 0, 0, 0}, a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, c, 4, 4, 0, sc, 0, sc);
+}
+
 template <class C, int KIND, bool CONV>
 __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, void *__restrict__ out,
@@ -305,11 +332,12 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
         dma16(isA ? ra : rb, voff[i], smem_base + slot * C::STAGE_BYTES + (isA ? j : C::ABLK + j) * 1024);
     };
 
-    i32x4 acc[C::FM][C::FN];
+    using Acc = std::conditional_t<KIND == KIND_B1F4, f32x4, i32x4>;
+    Acc acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
     const int64_t nk = ((int64_t)klen + C::BK - 1) / C::BK;
     const bool k_tail = (klen % C::BK) != 0;
@@ -446,6 +474,23 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                 step(std::integral_constant<int, 4>{});
                 step(std::integral_constant<int, 5>{});
                 step(std::integral_constant<int, 6>{});
+            } else if constexpr (KIND == KIND_B1F4) {
+                auto plane = [&](auto sc) {
+                    constexpr int st = decltype(sc)::value;
+                    i32x4 ea[C::FM];
+#pragma unroll
+                    for (int i = 0; i < C::FM; ++i) ea[i] = fp4_plane<st>(af[i]);
+#pragma unroll
+                    for (int j = 0; j < C::FN; ++j) {
+                        const i32x4 eb = fp4_plane<st>(bf[j]);
+#pragma unroll
+                        for (int i = 0; i < C::FM; ++i) acc[i][j] = mfma_fp4<st>(eb, ea[i], acc[i][j]);
+                    }
+                };
+                plane(std::integral_constant<int, 0>{});
+                plane(std::integral_constant<int, 1>{});
+                plane(std::integral_constant<int, 2>{});
+                plane(std::integral_constant<int, 3>{});
             } else {
 #pragma unroll
                 for (int i = 0; i < C::FM; ++i)
@@ -469,7 +514,14 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
         for (int j = 0; j < C::FN; ++j) {
             const int64_t n = n0 + wn * C::TN + j * 16 + (lane / 16) * 4;
             if (n >= N) continue;
-            i32x4 v = acc[i][j];
+            i32x4 v;
+            if constexpr (KIND == KIND_B1F4) {
+                // exact: the fp32 sums are integers below 2^24
+                v = i32x4{(int32_t)acc[i][j].x, (int32_t)acc[i][j].y, (int32_t)acc[i][j].z,
+                          (int32_t)acc[i][j].w};
+            } else {
+                v = acc[i][j];
+            }
             if constexpr (KIND == KIND_S4) v = v >> 8;
             if constexpr (KIND == KIND_B1) v = v >> 6;
             if constexpr (KIND == KIND_LINEAR) {
@@ -848,7 +900,7 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     case 5: return launch_one<M4, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     default: break;
     }
-    constexpr bool b1 = KIND == KIND_B1;
+    constexpr bool b1 = KIND == KIND_B1 || KIND == KIND_B1F4;
     switch (variant) {
     case 6:
         // int8 GEMM and linear layer: the four-wave large tile (same 256x256
@@ -895,6 +947,7 @@ hipError_t launch_mfma(int kind, int variant, const void *A, const void *B, void
     case KIND_LINEAR:
         return dispatch<KIND_LINEAR, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, ksplit, none, s);
     case KIND_B1: return dispatch<KIND_B1, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, ksplit, none, s);
+    case KIND_B1F4: return dispatch<KIND_B1F4, false>(variant, A, B, out, sx, sw, M, N, Kb, ldo, ksplit, none, s);
     default: return hipErrorInvalidValue;
     }
 }

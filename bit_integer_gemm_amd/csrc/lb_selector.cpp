@@ -33,10 +33,15 @@ struct SelEntry {
 #include "selector_table.inc"
 #include "selector_mlp.inc"
 
-// The pages' classifier (Research results item 3): 4 inputs (log2 M, log2 N,
-// log2 K each divided by 16, CU count divided by 256) -> three ReLU layers of
-// 128 -> 9 logits.  Weights trained offline on measured sweeps, stored as fp32
-// bit patterns.
+// The pages' selector network (Research results item 3): three ReLU layers of
+// 128 and one output per template, fed features of (M, N, K, CU count), one
+// network per operand type, weights trained offline on measured timings and
+// stored as fp32 bit patterns.  Features (standardised with the training
+// set's mean and spread): log2 M, log2 N, log2 K; per tile size (64, 128,
+// 256 square) log2 of its workgroup count, and for each workgroups-per-CU
+// figure it runs at (64: 2, 3, 4; 128: 2, 3; 256: 1) log2 of the number of
+// rounds ceil(tiles / (CU * per-CU)) and the fill of the last round.  Output v
+// is template v's predicted regret, log(t_v / t_fastest); lowest wins.
 float bits_to_float(uint32_t u)
 {
     float f;
@@ -55,36 +60,66 @@ void dense(const uint32_t *W, const uint32_t *b, const float *in, int fin, float
     }
 }
 
-void mlp_logits(int dtype, int64_t M, int64_t N, int64_t K, int cu, float *logits)
+int mlp_features(int64_t M, int64_t N, int64_t K, int cu, float *f)
 {
-    const uint32_t *W[4], *B[4];
+    static const int kTile[3] = {64, 128, 256};
+    static const int kPerCu[3][3] = {{2, 3, 4}, {2, 3, 0}, {1, 0, 0}};
+    int n = 0;
+    f[n++] = (float)std::log2((double)M);
+    f[n++] = (float)std::log2((double)N);
+    f[n++] = (float)std::log2((double)K);
+    for (int t = 0; t < 3; ++t) {
+        const int64_t b = kTile[t];
+        const int64_t T = ((M + b - 1) / b) * ((N + b - 1) / b);
+        f[n++] = (float)std::log2((double)T);
+        for (int o = 0; o < 3 && kPerCu[t][o] > 0; ++o) {
+            const int64_t slots = (int64_t)cu * kPerCu[t][o];
+            const int64_t R = (T + slots - 1) / slots;
+            f[n++] = (float)std::log2((double)R);
+            f[n++] = (float)((double)T / ((double)R * (double)slots));
+        }
+    }
+    return n;
+}
+
+void mlp_scores(int dtype, int64_t M, int64_t N, int64_t K, int cu, float *scores)
+{
+    const uint32_t *W[4], *B[4], *mu, *sd;
     switch (dtype) {
     case 0:
         W[0] = kMlpW0_0; W[1] = kMlpW0_1; W[2] = kMlpW0_2; W[3] = kMlpW0_3;
         B[0] = kMlpB0_0; B[1] = kMlpB0_1; B[2] = kMlpB0_2; B[3] = kMlpB0_3;
+        mu = kMlpMu0; sd = kMlpSd0;
         break;
     case 1:
         W[0] = kMlpW1_0; W[1] = kMlpW1_1; W[2] = kMlpW1_2; W[3] = kMlpW1_3;
         B[0] = kMlpB1_0; B[1] = kMlpB1_1; B[2] = kMlpB1_2; B[3] = kMlpB1_3;
+        mu = kMlpMu1; sd = kMlpSd1;
         break;
     default:
         W[0] = kMlpW2_0; W[1] = kMlpW2_1; W[2] = kMlpW2_2; W[3] = kMlpW2_3;
         B[0] = kMlpB2_0; B[1] = kMlpB2_1; B[2] = kMlpB2_2; B[3] = kMlpB2_3;
+        mu = kMlpMu2; sd = kMlpSd2;
         break;
     }
-    float x[4] = {(float)(std::log2((double)M) / 16.0), (float)(std::log2((double)N) / 16.0),
-                  (float)(std::log2((double)K) / 16.0), (float)(cu / 256.0)};
+    float x[LB_MLP_NFEAT];
+    const int nf = mlp_features(M, N, K, cu, x);
+    (void)nf;
+    for (int i = 0; i < LB_MLP_NFEAT; ++i) x[i] = (x[i] - bits_to_float(mu[i])) / bits_to_float(sd[i]);
     float h1[LB_MLP_HIDDEN], h2[LB_MLP_HIDDEN];
-    dense(W[0], B[0], x, 4, h1, LB_MLP_HIDDEN, true);
+    dense(W[0], B[0], x, LB_MLP_NFEAT, h1, LB_MLP_HIDDEN, true);
     dense(W[1], B[1], h1, LB_MLP_HIDDEN, h2, LB_MLP_HIDDEN, true);
     dense(W[2], B[2], h2, LB_MLP_HIDDEN, h1, LB_MLP_HIDDEN, true);
-    dense(W[3], B[3], h1, LB_MLP_HIDDEN, logits, LB_NUM_VARIANTS, false);
+    dense(W[3], B[3], h1, LB_MLP_HIDDEN, scores, LB_NUM_VARIANTS, false);
 }
 
+// The network decides unless LB_SELECTOR=table asks for the table of measured
+// labels (or the dtype has no trained network).
 bool use_mlp(int dtype)
 {
     const char *e = std::getenv("LB_SELECTOR");
-    return e && std::strcmp(e, "mlp") == 0 && dtype >= 0 && dtype < 3 && kMlpPresent[dtype];
+    if (e && std::strcmp(e, "table") == 0) return false;
+    return dtype >= 0 && dtype < 3 && kMlpPresent[dtype];
 }
 
 std::atomic<int> g_cu_cache[64];
@@ -149,16 +184,17 @@ void table_choice(int dtype, int64_t M, int64_t N, int64_t K, int *best, int *se
     *second = pts[bi].second;
 }
 
+// Lowest predicted regret, then the second lowest (ties to the lower index).
 void mlp_choice(int dtype, int64_t M, int64_t N, int64_t K, int cu, int *best, int *second)
 {
-    float lg[LB_NUM_VARIANTS];
-    mlp_logits(dtype, M, N, K, cu, lg);
+    float sc[LB_NUM_VARIANTS];
+    mlp_scores(dtype, M, N, K, cu, sc);
     int b0 = 0;
     for (int v = 1; v < LB_NUM_VARIANTS; ++v)
-        if (lg[v] > lg[b0]) b0 = v;
+        if (sc[v] < sc[b0]) b0 = v;
     int b1 = b0 == 0 ? 1 : 0;
     for (int v = 0; v < LB_NUM_VARIANTS; ++v)
-        if (v != b0 && lg[v] > lg[b1]) b1 = v;
+        if (v != b0 && sc[v] < sc[b1]) b1 = v;
     *best = b0;
     *second = b1;
 }

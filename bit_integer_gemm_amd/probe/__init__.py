@@ -1,0 +1,96 @@
+"""Measurements behind design decisions (a tool; not part of the GEMM library).
+
+1. Matrix-instruction issue rates on gfx950.  Times the int8 16x16x64 MFMA and the scaled 16x16x128 MFMA with FP8 e4m3,
+FP6 e3m2 and FP4 e2m1 operands, each wave issuing 16 independent accumulator
+chains, at 1, 2 and 4 waves per SIMD; operands hold realistic bits (uniform
+int8 bytes; random e3m2 codes; one bit plane per FP4 nibble, as the 1-bit GEMM
+feeds it).  These rates decide which matrix instruction a low-bit operand is
+worth converting to.
+
+2. Output-store bandwidth when all workgroups store at once, when only one
+XCD's do, and when one in eight of every XCD's do (256 KiB each, the int32
+tile of a 256 x 256 GEMM tile), to tell a per-XCD limit from a chip-wide one.
+
+  python -m bit_integer_gemm_amd.probe          # prints one JSON object
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "probe.hip")
+LIB = os.path.join(HERE, "libprobe.so")
+KINDS = {"int8_16x16x64": (0, 2 * 16 * 16 * 64), "fp8_e4m3_16x16x128": (1, 2 * 16 * 16 * 128),
+         "fp6_e3m2_16x16x128": (2, 2 * 16 * 16 * 128), "fp4_e2m1_16x16x128": (3, 2 * 16 * 16 * 128)}
+
+
+def build() -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", SRC, "-o", LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {SRC}:\n{r.stderr[-4000:]}")
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def measure(target_ms: float = 8.0) -> dict:
+    import torch
+    lib = ctypes.CDLL(LIB)
+    lib.mfma_rate_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.mfma_rate_run.restype = ctypes.c_float
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"cu": cu, "rates": {}}
+    for name, (kind, ops) in KINDS.items():
+        for wps in (1, 2, 4):
+            blocks = cu * wps          # 4 waves per workgroup = one per SIMD
+            buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            iters = 64
+            ms = lib.mfma_rate_run(kind, blocks, iters, ctypes.c_void_p(buf.data_ptr()))
+            if ms < 0:
+                raise RuntimeError(f"probe launch failed ({ms})")
+            iters = max(64, int(iters * target_ms / max(ms, 1e-3)))
+            best = min(lib.mfma_rate_run(kind, blocks, iters, ctypes.c_void_p(buf.data_ptr()))
+                       for _ in range(3))
+            n_inst = iters * 16 * wps            # per SIMD
+            out["rates"][f"{name}/waves_per_simd={wps}"] = {
+                "ns_per_instruction_per_simd": round(best * 1e6 / n_inst, 3),
+                "tops": round(ops * n_inst * 4 * cu / (best / 1e3) / 1e12, 1),
+                "iters": iters, "ms": round(best, 3)}
+            print(f"[probe] {name} waves/SIMD {wps}: {best * 1e6 / n_inst:.2f} ns per instruction per SIMD",
+                  flush=True)
+    return out
+
+
+def measure_stores(chunk_bytes: int = 256 << 10, reps: int = 5) -> dict:
+    """GB/s of the store probe: all 2048 workgroups (8 per CU) storing, those of
+    one XCD, and one in eight of every XCD's."""
+    import torch
+    lib = ctypes.CDLL(LIB)
+    lib.store_rate_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.store_rate_run.restype = ctypes.c_float
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = cu * 8
+    buf = torch.empty(blocks * chunk_bytes, dtype=torch.uint8, device="cuda")
+    out = {}
+    for mode, name, share in ((0, "all workgroups", 1.0), (1, "one XCD's workgroups", 1 / 8),
+                              (2, "one in eight of every XCD's workgroups", 1 / 8)):
+        ms = min(lib.store_rate_run(blocks, chunk_bytes, mode, ctypes.c_void_p(buf.data_ptr()))
+                 for _ in range(reps))
+        if ms < 0:
+            raise RuntimeError(f"store probe failed ({ms})")
+        nbytes = blocks * chunk_bytes * share
+        out[name] = {"bytes": int(nbytes), "us": round(ms * 1e3, 2), "GB_per_s": round(nbytes / (ms / 1e3) / 1e9, 1)}
+        print(f"[probe] stores, {name}: {nbytes / 2**20:.0f} MiB in {ms * 1e3:.1f} us", flush=True)
+    return out
+
+
+def main():
+    if not os.path.exists(LIB):
+        sys.exit(f"{LIB} not built: run __graft_entry__.build() or bit_integer_gemm_amd.probe.build()")
+    print(json.dumps({"mfma": measure(), "stores": measure_stores()}))

@@ -1,0 +1,158 @@
+// probe.hip -- measurements behind design decisions of the low-bit GEMM (not
+// part of the GEMM library).
+//
+// 1. Issue rate of the gfx950 matrix instructions a low-bit GEMM can run on, measured with realistic operand bits: int8 16x16x64 (uniform
+// random bytes, the int8 GEMM), and the scaled 16x16x128 instruction with FP8
+// e4m3, FP6 e3m2 (int4 values, which e3m2 holds exactly) and FP4 e2m1 (one
+// bit per nibble, the 1-bit GEMM's bit planes) operands.  Each wave keeps 16
+// independent accumulators, so the count is issue-bound, not latency-bound.
+//
+// 2. Write bandwidth of a GEMM-like output store when only some workgroups
+// store at a time: every workgroup writes its own contiguous 256 KiB (a
+// 256 x 256 int32 tile) with 16-byte stores, and a mask picks the ones that do
+// (all of them; those of one XCD; or 1 in 8 of every XCD's).  Whether the
+// store phase of a GEMM is bound per XCD or chip-wide decides whether
+// staggering tiles in time can hide it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum { R_I8 = 0, R_FP8 = 1, R_FP6 = 2, R_FP4 = 3 };
+
+__device__ inline uint32_t mix(uint32_t x)
+{
+    x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
+    return x;
+}
+
+// Operand bits for one lane: `words` 32-bit words in the instruction's format.
+template <int KIND>
+__device__ inline uint32_t operand_word(uint32_t s)
+{
+    const uint32_t r = mix(s);
+    if constexpr (KIND == R_I8) return r;                          // any byte is an int8
+    if constexpr (KIND == R_FP8) return r & 0x77777777u;           // e4m3 without NaN codes
+    if constexpr (KIND == R_FP6) return r;                         // every e3m2 code is finite
+    return r & 0x11111111u;                                        // e2m1 0.5 or 0: one bit plane
+}
+
+// The instructions are inline assembly with the accumulator tied to its
+// AGPRs: with the builtins the compiler rotates accumulators between register
+// files and pads the loop with moves and wait states, which it then measures.
+template <int KIND>
+__device__ inline void mma(f32x4 &acc, const i32x8 &a, const i32x8 &b, int one)
+{
+    if constexpr (KIND == R_FP8) {
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                     : "+a"(acc) : "v"(a), "v"(b), "v"(one));
+    } else if constexpr (KIND == R_FP6) {
+        const i32x6 a6 = {a[0], a[1], a[2], a[3], a[4], a[5]}, b6 = {b[0], b[1], b[2], b[3], b[4], b[5]};
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:3 blgp:3"
+                     : "+a"(acc) : "v"(a6), "v"(b6), "v"(one));
+    } else {
+        const i32x4 a4 = {a[0], a[1], a[2], a[3]}, b4 = {b[0], b[1], b[2], b[3]};
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+a"(acc) : "v"(a4), "v"(b4), "v"(one));
+    }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void rate_kernel(uint32_t seed, int iters, float *out)
+{
+    const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+    i32x8 a, b;
+    for (int d = 0; d < 8; ++d) {
+        a[d] = (int)operand_word<KIND>(seed ^ (gid * 16u + (uint32_t)d));
+        b[d] = (int)operand_word<KIND>(seed ^ (gid * 16u + 8u + (uint32_t)d) ^ 0x5bd1e995u);
+    }
+    float total = 0.f;
+    if constexpr (KIND == R_I8) {
+        i32x4 acc[16];
+        for (int q = 0; q < 16; ++q) acc[q] = i32x4{0, 0, 0, 0};
+        const i32x4 a4 = {a[0], a[1], a[2], a[3]}, b4 = {b[0], b[1], b[2], b[3]};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc[q]) : "v"(a4), "v"(b4));
+        }
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        for (int q = 0; q < 16; ++q) total += (float)(acc[q][0] + acc[q][1] + acc[q][2] + acc[q][3]);
+    } else {
+        f32x4 acc[16];
+        for (int q = 0; q < 16; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int one = 127;  // E8M0 scale 2^0
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) mma<KIND>(acc[q], a, b, one);
+        }
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        for (int q = 0; q < 16; ++q) total += acc[q][0] + acc[q][1] + acc[q][2] + acc[q][3];
+    }
+    out[gid] = total;
+}
+
+// Workgroup b writes bytes [b * chunk, (b + 1) * chunk) of out when it is
+// selected: mode 0 every workgroup, mode 1 those with b % 8 == 0 (consecutive
+// workgroups go round robin over the 8 XCDs, so: the CUs of one XCD), mode 2
+// those with (b / 8) % 8 == 0 (one in eight of every XCD's).
+__global__ __launch_bounds__(256) void store_kernel(i32x4 *out, int chunk_vec, int mode)
+{
+    const uint32_t b = blockIdx.x;
+    const bool on = mode == 0 || (mode == 1 && b % 8u == 0u) || (mode == 2 && (b / 8u) % 8u == 0u);
+    if (!on) return;
+    i32x4 *p = out + (size_t)b * (size_t)chunk_vec;
+    const i32x4 v = {(int)b, (int)threadIdx.x, 1, 2};
+    for (int i = threadIdx.x; i < chunk_vec; i += 256) p[i] = v;
+}
+
+extern "C" {
+
+// Launch `blocks` workgroups of store_kernel writing `chunk_bytes` each (a
+// multiple of 16) into out, which must hold blocks * chunk_bytes bytes.
+// Returns milliseconds between HIP events around the launch, or < 0 on error.
+float store_rate_run(int blocks, int chunk_bytes, int mode, void *out)
+{
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1.f;
+    (void)hipEventRecord(e0, 0);
+    hipLaunchKernelGGL(store_kernel, dim3(blocks), dim3(256), 0, 0, (i32x4 *)out, chunk_bytes / 16, mode);
+    (void)hipEventRecord(e1, 0);
+    if (hipEventSynchronize(e1) != hipSuccess) return -3.f;
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return hipGetLastError() == hipSuccess ? ms : -4.f;
+}
+
+
+// Launch `blocks` workgroups of 4 waves; each wave issues 16 * iters matrix
+// instructions of the given kind.  out must hold blocks * 256 floats.
+// Returns the elapsed milliseconds between HIP events around the launch, or a
+// negative value on a HIP error.
+float mfma_rate_run(int kind, int blocks, int iters, float *out)
+{
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1.f;
+    (void)hipEventRecord(e0, 0);
+    switch (kind) {
+    case R_I8: hipLaunchKernelGGL(rate_kernel<R_I8>, dim3(blocks), dim3(256), 0, 0, 12345u, iters, out); break;
+    case R_FP8: hipLaunchKernelGGL(rate_kernel<R_FP8>, dim3(blocks), dim3(256), 0, 0, 12345u, iters, out); break;
+    case R_FP6: hipLaunchKernelGGL(rate_kernel<R_FP6>, dim3(blocks), dim3(256), 0, 0, 12345u, iters, out); break;
+    case R_FP4: hipLaunchKernelGGL(rate_kernel<R_FP4>, dim3(blocks), dim3(256), 0, 0, 12345u, iters, out); break;
+    default: return -2.f;
+    }
+    (void)hipEventRecord(e1, 0);
+    if (hipEventSynchronize(e1) != hipSuccess) return -3.f;
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return hipGetLastError() == hipSuccess ? ms : -4.f;
+}
+
+}  // extern "C"

@@ -180,11 +180,21 @@ def run_sweep(dtype, out_path, Ms=None, Ns=None, Ks=None, check=True, log=print)
 
 def load_records(paths, auto=False):
     """Timings keyed by (dtype, M, N, K, variant): the nine variants, or with
-    auto=True the records of the library's own choice (variant "auto")."""
+    auto=True the records of the library's own choice (variant "auto").
+    Reads both record formats: one line per (shape, variant) from `run`, and
+    one line per shape with all nine times from `heldout`."""
     recs = {}
     for p in paths:
         for line in open(p):
             r = json.loads(line)
+            if isinstance(r.get("sec"), list):
+                if auto:
+                    if r.get("auto_sec") is not None:
+                        recs[(r["dtype"], r["M"], r["N"], r["K"], "auto")] = {"sec": r["auto_sec"]}
+                    continue
+                for v, t in enumerate(r["sec"]):
+                    recs[(r["dtype"], r["M"], r["N"], r["K"], v)] = {"sec": t}
+                continue
             if (r["variant"] == "auto") != auto:
                 continue
             recs[(r["dtype"], r["M"], r["N"], r["K"], r["variant"])] = r
@@ -298,6 +308,29 @@ K_RANGE = {"s8": (256, 16384), "s4": (256, 16384), "b1": (1024, 65536)}
 K_ALIGN = {"s8": 16, "s4": 32, "b1": 128}
 
 
+def train_shapes(dtype, n=500, seed=31337):
+    """Seeded random shapes for building the selection (training data beside
+    the grid): log-uniform M, N in 48..16384 and K over the dtype's range,
+    aligned, at most 2^40 multiply-adds.  Drawn from another seed than the
+    held-out shapes, so the two sets share no shape by construction."""
+    import numpy as np
+    g = np.random.Generator(np.random.PCG64(seed + DTYPES[dtype]))
+    lo, hi = K_RANGE[dtype]
+    al = K_ALIGN[dtype]
+    out = []
+    while len(out) < n:
+        M = int(round(2 ** g.uniform(math.log2(48), 14)))
+        N = int(round(2 ** g.uniform(math.log2(48), 14)))
+        K = max(al, int(round(2 ** g.uniform(math.log2(lo), math.log2(hi)) / al)) * al)
+        if M * N * K <= (1 << 40):
+            out.append((M, N, K))
+    return out
+
+
+def grid_shapes(dtype):
+    return [(M, N, K) for K in GRID_K[dtype] for M in GRID_MN for N in GRID_MN]
+
+
 def heldout_shapes(dtype, n_random=80, seed=20260):
     """Seeded off-grid shapes for scoring the selection on data it was not
     built from: `n_random` shapes log-uniform over the sweep's range (M, N in
@@ -338,11 +371,12 @@ def heldout_shapes(dtype, n_random=80, seed=20260):
     return shapes
 
 
-def run_heldout(dtype, out_path, shapes=None, log=print):
-    """Time the nine variants, twice (in opposite orders, keeping each one's
-    faster median), plus the library's automatic path, on each held-out
-    shape; record what the table and the classifier select.  Also checks that
-    every variant returns the same C as the default."""
+def run_heldout(dtype, out_path, shapes=None, log=print, passes=2, auto=True):
+    """Time the nine variants, `passes` times (in alternating orders, keeping
+    each one's faster median), plus the library's automatic path, on each
+    shape (default: the held-out shapes); record what the table and the
+    classifier select.  Also checks that every variant returns the same C as
+    the default."""
     import torch
     import bit_integer_gemm_amd as lb
     lb.load()
@@ -372,18 +406,18 @@ def run_heldout(dtype, out_path, shapes=None, log=print):
         C = torch.empty(M, N, dtype=torch.int32, device="cuda")
         call(A, B, C, DEFAULT)
         ref = C.clone()
-        sel_table = lb.lb_select_variant(DTYPES[dtype], M, N, K, 0)
+        sel_net = lb.lb_select_variant(DTYPES[dtype], M, N, K, 0)
         old = os.environ.get("LB_SELECTOR")
-        os.environ["LB_SELECTOR"] = "mlp"
-        sel_mlp = lb.lb_select_variant(DTYPES[dtype], M, N, K, 0)
+        os.environ["LB_SELECTOR"] = "table"
+        sel_table = lb.lb_select_variant(DTYPES[dtype], M, N, K, 0)
         if old is None:
             os.environ.pop("LB_SELECTOR")
         else:
             os.environ["LB_SELECTOR"] = old
-        order = list(range(9)) + ["auto"]
+        order = list(range(9)) + (["auto"] if auto else [])
         best = {}
         agree = True
-        for rnd in range(2):
+        for rnd in range(passes):
             for v in (order if rnd == 0 else order[::-1]):
                 vv = lb.LB_AUTO if v == "auto" else v
                 t, _ = time_calls(lambda: call(A, B, C, vv), torch)
@@ -391,34 +425,62 @@ def run_heldout(dtype, out_path, shapes=None, log=print):
                 if rnd == 0:
                     agree = agree and bool(torch.equal(C, ref))
         rec = {"dtype": dtype, "M": M, "N": N, "K": K, "sec": [best[v] for v in range(9)],
-               "auto_sec": best["auto"], "table": list(sel_table), "mlp": list(sel_mlp),
+               "auto_sec": best.get("auto"), "table": list(sel_table), "network": list(sel_net),
                "agree": agree}
         f.write(json.dumps(rec) + "\n")
         f.flush()
-        log(f"[heldout] {dtype} {M}x{N}x{K} table v{sel_table[0]} mlp v{sel_mlp[0]} "
-            + " ".join(f"v{v}:{best[v] * 1e6:.1f}" for v in range(9)) + f" auto:{best['auto'] * 1e6:.1f}")
+        log(f"[heldout] {dtype} {M}x{N}x{K} network v{sel_net[0]} table v{sel_table[0]} "
+            + " ".join(f"v{v}:{best[v] * 1e6:.1f}" for v in range(9))
+            + (f" auto:{best['auto'] * 1e6:.1f}" if auto else ""))
         if not agree:
             raise RuntimeError(f"a variant disagrees with the default at {dtype} {M}x{N}x{K}")
         del A, B, C, ref
     f.close()
 
 
-def score_heldout(paths, eps=EPS, default=DEFAULT):
-    """Scores of the table and the classifier on held-out timings: violations
-    (selected more than eps slower than the default), top-2 (the fastest is
-    among the two predicted), top-1 within eps, selected / fastest time, and
-    the speedups over the default and over the best single fixed variant
-    (chosen on these shapes, so that comparison favours the fixed variant)."""
+def library_choices(rows, cu=256):
+    """What the built library selects for each row's shape, in both modes
+    (host-only queries, no GPU needed): the network (the default) and the
+    table of measured labels (LB_SELECTOR=table)."""
+    import bit_integer_gemm_amd as lb
+    lb.load()
+    old = os.environ.pop("LB_SELECTOR", None)
+    try:
+        for r in rows:
+            r["network"] = list(lb.lb_select_variant(DTYPES[r["dtype"]], r["M"], r["N"], r["K"], cu))
+        os.environ["LB_SELECTOR"] = "table"
+        for r in rows:
+            r["table"] = list(lb.lb_select_variant(DTYPES[r["dtype"]], r["M"], r["N"], r["K"], cu))
+    finally:
+        os.environ.pop("LB_SELECTOR", None)
+        if old is not None:
+            os.environ["LB_SELECTOR"] = old
+    return rows
+
+
+def score_heldout(paths, eps=EPS, default=DEFAULT, query_library=True):
+    """Scores of the selection on held-out timings: violations (selected more
+    than eps slower than the default), top-2 (the fastest is among the two
+    predicted), top-1 within eps, selected / fastest time, and the speedups
+    over the default and over the best single fixed variant (chosen on these
+    shapes, so that comparison favours the fixed variant).  With
+    query_library the choices are what the built library selects now (network
+    and table); otherwise the ones recorded with the timings."""
     rows = [json.loads(line) for p in paths for line in open(p)]
     if not rows:
         return {}
+    if query_library:
+        library_choices(rows)
+    else:
+        for r in rows:
+            r["network"] = r.get("network", r.get("mlp"))
 
     def gm(xs):
         return math.exp(sum(math.log(x) for x in xs) / len(xs))
     out = {"shapes": len(rows), "eps": eps, "default_variant": default}
     fixed = min(range(9), key=lambda v: gm([r["sec"][v] / min(r["sec"]) for r in rows]))
     out["best_fixed_variant"] = fixed
-    for who in ("table", "mlp"):
+    for who in ("network", "table"):
         t_sel = [r["sec"][r[who][0]] for r in rows]
         best = [min(r["sec"]) for r in rows]
         fastest = [min(range(9), key=lambda v: (r["sec"][v], v)) for r in rows]
@@ -436,8 +498,10 @@ def score_heldout(paths, eps=EPS, default=DEFAULT):
             "speedup_vs_best_fixed": {"geomean": gm([r["sec"][fixed] / ts for r, ts in zip(rows, t_sel)]),
                                       "min": min(r["sec"][fixed] / ts for r, ts in zip(rows, t_sel))},
         }
+    # the automatic path (recorded with the library the timings were taken
+    # with: its choice, plus any two-launch split, K bands or stream-K)
     sp = [r["sec"][default] / r["auto_sec"] for r in rows]
-    sp_sel = [r["sec"][r["table"][0]] / r["auto_sec"] for r in rows]
+    sp_sel = [r["sec"][r["network"][0]] / r["auto_sec"] for r in rows]
     out["automatic_path"] = {
         "speedup_vs_default": {"geomean": gm(sp), "min": min(sp), "max": max(sp)},
         "speedup_vs_selected_variant": {"geomean": gm(sp_sel), "min": min(sp_sel), "max": max(sp_sel)},
@@ -466,13 +530,21 @@ def main(argv=None):
     h = sub.add_parser("heldout")
     h.add_argument("--dtype", choices=sorted(DTYPES), default="s8")
     h.add_argument("--out", required=True)
+    h.add_argument("--set", choices=("heldout", "train", "grid"), default="heldout",
+                   help="held-out shapes (two passes plus the automatic path), or the "
+                        "training shapes / the grid (one pass, variants only)")
     sh = sub.add_parser("score-heldout")
     sh.add_argument("files", nargs="+")
     sh.add_argument("--json", help="write the report here")
     a = ap.parse_args(argv)
     if a.cmd == "heldout":
         t0 = time.time()
-        run_heldout(a.dtype, a.out, log=lambda s: print(s, flush=True))
+        if a.set == "heldout":
+            run_heldout(a.dtype, a.out, log=lambda s: print(s, flush=True))
+        else:
+            shapes = train_shapes(a.dtype) if a.set == "train" else grid_shapes(a.dtype)
+            run_heldout(a.dtype, a.out, shapes=shapes, passes=1, auto=False,
+                        log=lambda s: print(s, flush=True))
         print(f"[heldout] done in {time.time() - t0:.1f} s", flush=True)
     elif a.cmd == "score-heldout":
         rep = score_heldout(a.files)

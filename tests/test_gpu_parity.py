@@ -143,30 +143,57 @@ def test_extreme_values_at_max_k():
         assert (run("b1", fives, aas, v) == 0).all()
 
 
-B1_PASS_K_CASE = (17, 9, lb.B1_PASS_K)
+@pytest.fixture
+def b1_route():
+    """Select the 1-bit route (LB_B1_ROUTE) for one test and restore it after."""
+    old = os.environ.get("LB_B1_ROUTE")
+
+    def use(route):
+        os.environ["LB_B1_ROUTE"] = route
+    yield use
+    if old is None:
+        os.environ.pop("LB_B1_ROUTE", None)
+    else:
+        os.environ["LB_B1_ROUTE"] = old
 
 
-@functools.lru_cache(maxsize=1)
-def b1_pass_k_case():
-    M, N, K = B1_PASS_K_CASE
+@functools.lru_cache(maxsize=2)
+def b1_pass_k_case(route):
+    M, N, K = 17, 9, lb.B1_PASS_K[route]
     A, B = inputs.b1_rows(M, K, 31), inputs.b1_rows(N, K, 32)
     return A, B, oracle.gemm_b1(A, B, K)
 
 
+@pytest.mark.parametrize("route", ["fp4", "int8"])
 @pytest.mark.parametrize("variant", list(range(9)))
-def test_b1_at_longest_single_pass_k(variant):
-    """The longest 1-bit K one kernel pass covers, where the kernel's
-    accumulator (64 per matching bit pair) comes within 8192 of the int32
-    limit: all ones give K exactly, and random bits match the oracle."""
-    M, N, K = B1_PASS_K_CASE
-    print(f"[parity] b1 K={K} v{variant}", flush=True)
+def test_b1_at_longest_single_pass_k(b1_route, route, variant):
+    """The longest 1-bit K one kernel pass covers, on both routes: on the FP4
+    route the fp32 accumulator reaches 2^24, the last integer fp32 counts
+    exactly; on the int8 route the accumulator (64 per matching bit pair) comes
+    within 8192 of the int32 limit.  All ones give K exactly, and random bits
+    match the oracle."""
+    b1_route(route)
+    A, B, want = b1_pass_k_case(route)
+    M, N, K = A.shape[0], B.shape[0], lb.B1_PASS_K[route]
+    print(f"[parity] b1 {route} K={K} v{variant}", flush=True)
     ones = np.full((M, K // 32), 0xFFFFFFFF, np.uint32)
     assert (run("b1", ones, ones[:N], variant) == K).all()
-    A, B, want = b1_pass_k_case()
     np.testing.assert_array_equal(run("b1", A, B, variant), want)
 
 
-B1_LONG_K_CASE = (17, 9, (1 << 26) + 384)   # three K bands
+@pytest.mark.parametrize("variant", [lb.LB_AUTO] + list(range(9)))
+def test_b1_int8_route_small_shapes(b1_route, variant):
+    """The int8 route of the 1-bit GEMM (weighted bit planes on the int8
+    instruction), kept for A/B measurement, against the oracle."""
+    b1_route("int8")
+    for i, (M, N, K) in enumerate(SMALL["b1"] + [(256, 300, 8192)]):
+        print(f"[parity] b1 int8 route v{variant} M={M} N={N} K={K}", flush=True)
+        A, B = make("b1", M, N, K, 600 + 10 * i)
+        np.testing.assert_array_equal(run("b1", A, B, variant, K), ref("b1", A, B, K),
+                                      err_msg=f"b1 int8 route v{variant} {M}x{N}x{K}")
+
+
+B1_LONG_K_CASE = (17, 9, (1 << 26) + 384)   # five K bands on the FP4 route, three on the int8 route
 
 
 @functools.lru_cache(maxsize=1)
@@ -176,19 +203,21 @@ def b1_long_k_case():
     return A, B, oracle.gemm_b1(A, B, K)
 
 
+@pytest.mark.parametrize("route", ["fp4", "int8"])
 @pytest.mark.parametrize("variant", [lb.LB_AUTO] + list(range(9)))
-def test_b1_long_k_runs_as_bands(variant):
-    """1-bit K beyond one pass (here 2^26 + 384 bits, three bands), for every
-    variant and the automatic choice: the bands' counts add up exactly."""
+def test_b1_long_k_runs_as_bands(b1_route, route, variant):
+    """1-bit K beyond one pass (here 2^26 + 384 bits), for every variant and
+    the automatic choice, on both routes: the bands' counts add up exactly."""
+    b1_route(route)
     M, N, K = B1_LONG_K_CASE
-    print(f"[parity] b1 long K={K} v{variant}", flush=True)
+    print(f"[parity] b1 {route} long K={K} v{variant}", flush=True)
     A, B, want = b1_long_k_case()
     np.testing.assert_array_equal(run("b1", A, B, variant), want)
 
 
 @pytest.mark.parametrize("variant", [lb.LB_AUTO, 0, 6, 7])
 def test_b1_at_max_k(variant):
-    """The largest 1-bit K the boundary accepts (2^27 - 128 bits, four bands):
+    """The largest 1-bit K the boundary accepts (2^27 - 128 bits, eight bands):
     all ones give K, and complementary bit patterns give 0 and K/2."""
     M, N, K = 17, 9, lb.K_MAX[lb.LB_B1]
     print(f"[parity] b1 K={K} v{variant}", flush=True)
@@ -472,10 +501,12 @@ def test_graph_capture_replays_match_eager():
 # then the remaining columns)
 # ---------------------------------------------------------------------------
 
-def splits(dtype_code, M, N, K):
+def splits(dtype_code, M, N, K, v=None):
     """Whether the library's automatic choice runs (M, N, K) as two launches:
-    a large-tile variant whose last round of tiles fills at most half the CUs."""
-    v = lb.lb_select_variant(dtype_code, M, N, K, 0)[0]
+    a large-tile variant (v, when LB_AUTO_VARIANT forces it) whose last round of
+    tiles fills at most half the CUs."""
+    if v is None:
+        v = lb.lb_select_variant(dtype_code, M, N, K, 0)[0]
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     T = -(-M // 256) * -(-N // 256)
     return v >= 6 and T > cu and T % cu != 0 and 2 * (T % cu) <= cu
@@ -483,26 +514,30 @@ def splits(dtype_code, M, N, K):
 
 # Column bands (19 tile columns over 16 tile rows), and row bands (19 tile rows
 # over 16 tile columns, where no column band fills whole rounds); ragged edges.
-@pytest.mark.parametrize("kind,M,N,K", [
-    ("s8", 4096, 4864, 4096), ("s8", 4000, 4810, 4096),
-    ("s4", 4096, 4864, 4096), ("s4", 4000, 4810, 4096),
-    ("b1", 4000, 4810, 4096),
-    ("s8", 4864, 4096, 4096), ("s8", 4810, 4000, 4096),
-    ("s4", 4810, 4000, 4096), ("b1", 4810, 4000, 4096),
+# The selector avoids a large tile whose last round is nearly empty, so the
+# large tiles (the 2-stage one, variant 6, and the default, 7) are forced.
+@pytest.mark.parametrize("kind,M,N,K,v", [
+    ("s8", 4096, 4864, 4096, 6), ("s8", 4000, 4810, 4096, 7),
+    ("s4", 4096, 4864, 4096, 6), ("s4", 4000, 4810, 4096, 7),
+    ("b1", 4000, 4810, 4096, 6),
+    ("s8", 4864, 4096, 4096, 6), ("s8", 4810, 4000, 4096, 7),
+    ("s4", 4810, 4000, 4096, 6), ("b1", 4810, 4000, 4096, 7),
 ])
-def test_auto_split_launches_match_oracle(kind, M, N, K):
-    print(f"[parity] split {kind} {M}x{N}x{K}", flush=True)
+def test_auto_split_launches_match_oracle(forced_auto_variant, kind, M, N, K, v):
+    print(f"[parity] split {kind} {M}x{N}x{K} v{v}", flush=True)
+    forced_auto_variant(v)
     code = {"s8": lb.LB_S8, "s4": lb.LB_S4, "b1": lb.LB_B1}[kind]
-    assert splits(code, M, N, K), "shape no longer exercises the two-launch path"
+    assert splits(code, M, N, K, v), "shape no longer exercises the two-launch path"
     A, B = make(kind, M, N, K, 2024)
     got = run(kind, A, B, lb.LB_AUTO, K)
     np.testing.assert_array_equal(got, ref(kind, A, B, K))
 
 
 @pytest.mark.parametrize("M,N", [(4000, 4810), (4810, 4000)])
-def test_auto_split_linear_matches_oracle(M, N):
+def test_auto_split_linear_matches_oracle(forced_auto_variant, M, N):
     K = 4096
-    assert splits(lb.LB_S8, M, N, K)
+    forced_auto_variant(6)
+    assert splits(lb.LB_S8, M, N, K, 6)
     X, W = inputs.s8_rows(M, K, 71), inputs.s8_rows(N, K, 72)
     sx, sw = inputs.scales(M, 73), inputs.scales(N, 74)
     assert_rel(run_linear(X, W, sx, sw, lb.LB_AUTO), oracle.linear_s8(X, W, sx, sw))
@@ -514,7 +549,7 @@ def test_auto_split_linear_matches_oracle(M, N):
 # ---------------------------------------------------------------------------
 
 KB_PER = {"s8": 1, "s4": 2, "b1": 8}   # elements per byte
-ALPHA = {"s8": 2.5, "s4": 2.3, "b1": 1.25}
+ALPHA = {"s8": 2.5, "s4": 2.3, "b1": 0.83}   # 1-bit: the FP4 route (the default)
 
 
 def k_bands(kind, M, N, K, v=None):
@@ -617,14 +652,15 @@ def test_forced_variant_reaches_the_linear_layer(forced_auto_variant):
 
 
 @pytest.mark.parametrize("kind,M,N,K", [("s8", 64, 64, 8192), ("s8", 4000, 4810, 4096)])
-def test_graph_capture_of_automatic_launches(kind, M, N, K):
+def test_graph_capture_of_automatic_launches(forced_auto_variant, kind, M, N, K):
     """The automatic path's extra launches (the zeroing of C before K bands, or
     the second launch of a two-launch split) captured into a HIP graph: every
     replay, with eager work and a clobbered C in between, reproduces the oracle."""
     if (M, N) == (64, 64):
         assert k_bands(kind, M, N, K) >= 2
     else:
-        assert splits(lb.LB_S8, M, N, K)
+        forced_auto_variant(6)
+        assert splits(lb.LB_S8, M, N, K, 6)
     A, B = make(kind, M, N, K, 5151)
     dA, dB = to_dev(A), to_dev(B)
     want = oracle.gemm_s8(A, B)
@@ -647,3 +683,4 @@ def test_graph_capture_of_automatic_launches(kind, M, N, K):
         g.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(C.cpu().numpy(), want, err_msg=f"replay {r}")
+

@@ -1,10 +1,11 @@
 """CPU tests of the variant selector (host logic only; no kernel is launched).
 
-Table mode: every measured shape must map to its own label, off-grid shapes to
-the label of the nearest measured shape in log2 space, computed here
-independently from the generated table text.  Classifier mode (LB_SELECTOR=mlp):
-the library's C++ forward pass must pick the same top-2 variants as a numpy
-forward pass over the same exported weights.
+Network mode (the default): the library's C++ forward pass must pick the same
+two templates (lowest predicted regrets) as a numpy forward pass over the same
+exported weights, and the features must match values worked out by hand.
+Table mode (LB_SELECTOR=table): every measured shape must map to its own label,
+off-grid shapes to the label of the nearest measured shape in log2 space,
+computed here independently from the generated table text.
 """
 import ctypes
 import math
@@ -46,12 +47,19 @@ def test_table_has_all_dtypes_and_valid_labels():
         assert 0 <= b < 9 and 0 <= s < 9 and b != s
 
 
-def test_measured_shapes_map_to_their_labels():
+@pytest.fixture
+def table_mode():
+    os.environ["LB_SELECTOR"] = "table"
+    yield
+    del os.environ["LB_SELECTOR"]
+
+
+def test_measured_shapes_map_to_their_labels(table_mode):
     for d, lm, ln, k, b, s in table_entries():
         assert lb.lb_select_variant(d, 2 ** lm, 2 ** ln, k, 256) == (b, s)
 
 
-def test_off_grid_shapes_take_nearest_label():
+def test_off_grid_shapes_take_nearest_label(table_mode):
     ents = table_entries()
     g = np.random.Generator(np.random.PCG64(5))
     for _ in range(300):
@@ -83,35 +91,56 @@ def test_device_query_fails_cleanly_without_gpu():
     assert lb.load().lb_select_variant(0, 64, 64, 64, 0, ctypes.byref(b), None) == lb.LB_ERR_HIP
 
 
-def test_classifier_matches_numpy_forward():
-    weights = selector_mlp.read_inc()
-    assert set(weights) == {0, 1, 2}
-    for code, ws in weights.items():
-        assert [W.shape for W, _ in ws] == [(128, 4), (128, 128), (128, 128), (9, 128)]
+def test_network_matches_numpy_forward():
+    nets = selector_mlp.read_inc()
+    assert set(nets) == {0, 1, 2}
+    for code, (ws, mu, sd) in nets.items():
+        assert [W.shape for W, _ in ws] == [(128, 18), (128, 128), (128, 128), (9, 128)]
+        assert mu.shape == sd.shape == (18,) and (sd > 0).all()
     g = np.random.Generator(np.random.PCG64(9))
-    os.environ["LB_SELECTOR"] = "mlp"
-    try:
-        checked = 0
-        for _ in range(400):
-            d = int(g.integers(0, 3))
-            M, N, K = (int(2 ** g.uniform(5, 15)) for _ in range(3))
-            lg = selector_mlp.forward_np(weights[d], selector_mlp.features(M, N, K, 256))
-            order = np.argsort(-lg)
-            if lg[order[0]] - lg[order[1]] < 1e-4 or lg[order[1]] - lg[order[2]] < 1e-4:
-                continue   # near-tie: fp32 summation order may legitimately flip it
-            assert lb.lb_select_variant(d, M, N, K, 256) == (int(order[0]), int(order[1])), (d, M, N, K)
-            checked += 1
-        assert checked > 300
-    finally:
-        del os.environ["LB_SELECTOR"]
+    checked = 0
+    for _ in range(400):
+        d = int(g.integers(0, 3))
+        M, N, K = (int(2 ** g.uniform(5, 15)) for _ in range(3))
+        ws, mu, sd = nets[d]
+        sc = selector_mlp.forward_np(ws, mu, sd, selector_mlp.features(M, N, K, 256))
+        order = np.argsort(sc, kind="stable")
+        if sc[order[1]] - sc[order[0]] < 1e-4 or sc[order[2]] - sc[order[1]] < 1e-4:
+            continue   # near-tie: fp32 summation order may legitimately flip it
+        assert lb.lb_select_variant(d, M, N, K, 256) == (int(order[0]), int(order[1])), (d, M, N, K)
+        assert selector_mlp.choose(nets[d], M, N, K) == (int(order[0]), int(order[1]))
+        checked += 1
+    assert checked > 300
 
 
-def test_classifier_layer_math_by_hand():
-    """One hand-built two-unit layer through forward_np: the reference itself is pinned."""
+def test_network_features_by_hand():
+    """The 18 features at 4096 x 4096 x 4096 on 256 CUs, worked out by hand:
+    tile 64: 4096 tiles; 2 per CU -> 8 full rounds; 3 per CU -> 6 rounds, the
+    last 1/3 full (fill 4096 / 4608); 4 per CU -> 4 rounds.  Tile 128: 1024
+    tiles; 2 per CU -> 2 rounds; 3 per CU -> 2 rounds, fill 1024 / 1536.  Tile
+    256: 256 tiles, one round."""
+    f = selector_mlp.features(4096, 4096, 4096, 256)
+    want = [12, 12, 12,
+            12, 3, 1.0, math.log2(6), 4096 / 4608, 2, 1.0,
+            10, 1, 1.0, 1, 1024 / 1536,
+            8, 0, 1.0]
+    assert len(f) == selector_mlp.NFEAT == 18
+    np.testing.assert_allclose(f, want, rtol=0, atol=1e-12)
+    # a ragged shape: 300 x 70 -> tile 64: 5 x 2 = 10 tiles, one round at 2/CU, fill 10/512
+    f = selector_mlp.features(300, 70, 1000, 256)
+    assert f[3] == math.log2(10) and f[4] == 0 and f[5] == 10 / 512
+
+
+def test_network_layer_math_by_hand():
+    """One hand-built two-unit network through forward_np, standardisation
+    included: the reference itself is pinned."""
     W = np.array([[1.0, -2.0], [0.5, 0.5]], np.float32)
     b = np.array([0.25, -3.0], np.float32)
     W2 = np.array([[2.0, 1.0]], np.float32)
-    out = selector_mlp.forward_np([(W, b), (W2, np.zeros(1, np.float32))], [3.0, 1.0])
+    mu = np.array([1.0, -1.0], np.float32)
+    sd = np.array([2.0, 1.0], np.float32)
+    # standardised input ((7 - 1) / 2, (0 + 1) / 1) = (3, 1)
+    out = selector_mlp.forward_np([(W, b), (W2, np.zeros(1, np.float32))], mu, sd, [7.0, 0.0])
     # hidden = relu([3 - 2 + 0.25, 1.5 + 0.5 - 3]) = [1.25, 0]; out = 2 * 1.25
     assert out.tolist() == [2.5]
 
@@ -147,18 +176,18 @@ def test_repeated_queries_and_mode_switches_agree():
     query in that mode gives (the mode is part of what is remembered)."""
     shapes = [(d, 2 ** a + 3, 2 ** b + 5, 256 * (1 + k)) for d in range(3) for a, b, k in
               ((6, 9, 0), (10, 7, 3), (13, 12, 15), (8, 14, 31))]
-    table = {s: lb.lb_select_variant(*s, 256) for s in shapes}
-    os.environ["LB_SELECTOR"] = "mlp"
+    net = {s: lb.lb_select_variant(*s, 256) for s in shapes}
+    os.environ["LB_SELECTOR"] = "table"
     try:
-        mlp = {s: lb.lb_select_variant(*s, 256) for s in shapes}
+        table = {s: lb.lb_select_variant(*s, 256) for s in shapes}
         for _ in range(3):
             for s in shapes:
-                assert lb.lb_select_variant(*s, 256) == mlp[s]
+                assert lb.lb_select_variant(*s, 256) == table[s]
     finally:
         del os.environ["LB_SELECTOR"]
     for _ in range(3):
         for s in shapes:
-            assert lb.lb_select_variant(*s, 256) == table[s]
+            assert lb.lb_select_variant(*s, 256) == net[s]
     # the table answers still follow the nearest-shape rule checked above
     ents = table_entries()
     for (d, M, N, K), got in table.items():
@@ -168,15 +197,15 @@ def test_repeated_queries_and_mode_switches_agree():
         best = min(dist(e) for e in cand)
         assert got in {(e[4], e[5]) for e in cand if abs(dist(e) - best) < 1e-12}
     # the two modes really differ somewhere, so the test can see a stale answer
-    assert any(table[s] != mlp[s] for s in shapes)
+    assert any(table[s] != net[s] for s in shapes)
 
 
 def test_sweep_records_of_the_automatic_path(tmp_path):
     """Sweep files may hold records of the library's own choice (variant
-    "auto"): labels and the classifier's loader ignore them, and the evaluation
-    reports the automatic path against the default and the selected variant."""
+    "auto"): labels ignore them, and the evaluation reports the automatic path
+    against the default and the selected variant."""
     import json
-    from bit_integer_gemm_amd import selector_mlp, sweep
+    from bit_integer_gemm_amd import sweep
     p = tmp_path / "run.jsonl"
     recs = []
     for M in (64, 128):
@@ -190,7 +219,6 @@ def test_sweep_records_of_the_automatic_path(tmp_path):
     p.write_text("\n".join(json.dumps(r) for r in recs) + "\n")
     lab = sweep.labels(sweep.load_records([str(p)]))
     assert lab[("s8", 64, 64, 256)][:2] == (2, 0)
-    assert set(selector_mlp.load_sweep([str(p)])["s8"]) == {(64, 64, 256), (128, 64, 256)}
     rep = sweep.evaluate(None, [str(p)])
     assert rep["shapes"] == 2 and rep["violations_slower_than_default"] == 0
     a = rep["automatic_path"]
@@ -199,3 +227,41 @@ def test_sweep_records_of_the_automatic_path(tmp_path):
     # against the adjacent timing of the selected variant (5.0), not the run's (4.0)
     assert abs(a["speedup_vs_selected_variant"]["geomean"] - 2.5) < 1e-9
     assert a["slower_than_default"] == 0
+
+
+def test_per_shape_records_and_heldout_scores(tmp_path):
+    """Per-shape records (all nine times in one line, as the held-out and
+    training runs write them) load for labels and for the network's trainer,
+    and the held-out scores count violations, top-2 and the time ratios."""
+    import json
+    from bit_integer_gemm_amd import sweep
+    p = tmp_path / "heldout.jsonl"
+    rows = []
+    # shape 1: selected 3 is fastest; shape 2: selected 0 is 1.5x the fastest (5)
+    # and slower than the default; shape 3: selected 7 (the default) second-fastest
+    for (M, t, sel) in ((100, [9, 9, 9, 2, 9, 9, 9, 9, 9], (3, 1)), (200, [3, 9, 9, 9, 9, 2, 9, 2.5, 9], (0, 1)),
+                        (300, [9, 9, 9, 9, 9, 9, 9, 2.2, 2], (7, 1))):
+        rows.append({"dtype": "s8", "M": M, "N": 64, "K": 256, "sec": [float(x) for x in t],
+                     "auto_sec": 2.0, "table": list(sel), "network": list(sel), "agree": True})
+    p.write_text("\n".join(json.dumps(r) for r in rows) + "\n")
+    recs = sweep.load_records([str(p)])
+    assert recs[("s8", 100, 64, 256, 3)]["sec"] == 2.0
+    assert set(selector_mlp.load([str(p)])["s8"]) == {(100, 64, 256), (200, 64, 256), (300, 64, 256)}
+    rep = sweep.score_heldout([str(p)], query_library=False)
+    t = rep["table"]
+    assert t["violations_slower_than_default"] == 1            # shape 2: 3 > 1.02 * 2.5
+    assert abs(t["top2_accuracy"] - 1 / 3) < 1e-12             # only shape 1 has the fastest in its pair
+    assert abs(t["selected_over_fastest_time"]["worst"] - 1.5) < 1e-12
+    assert rep["all_variants_agree"]
+
+
+def test_training_and_heldout_shapes_are_disjoint():
+    from bit_integer_gemm_amd import sweep
+    for d in ("s8", "s4", "b1"):
+        held = sweep.heldout_shapes(d)
+        train = sweep.train_shapes(d)
+        assert len(held) == 100 and len(train) == 500
+        assert not set(held) & set(train)
+        assert not set(held) & set(sweep.grid_shapes(d))
+        for M, N, K in held + train:
+            assert K % sweep.K_ALIGN[d] == 0 and M * N * K <= 1 << 40
