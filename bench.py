@@ -352,6 +352,9 @@ def main():
                     help="force one kernel variant (0..8) instead of the library's choice (A/B profiling)")
     ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"), default=None,
                     help="override M, N, K of a GEMM workload (A/B profiling)")
+    ap.add_argument("--lib", default=None,
+                    help="load this build of the library instead of the package's (A/B profiling builds "
+                         "from `python -m bit_integer_gemm_amd._build --ab NAME`)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (the reference for HBM byte counters) and exit")
     args = ap.parse_args()
@@ -373,6 +376,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
         return
     import bit_integer_gemm_amd as lb
+    if args.lib:
+        lb.load(os.path.abspath(args.lib))
     lb.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     props = torch.cuda.get_device_properties(0)

@@ -3,6 +3,11 @@
 Usage: ``python -m bit_integer_gemm_amd._build`` (or ``build()`` from Python).
 Every HIP/C++ source under ``csrc/`` is compiled for gfx950 only and linked
 into one library exporting the C ABI of ``include/lb_gemm.h``.
+
+``python -m bit_integer_gemm_amd._build --ab NAME`` builds an A/B profiling
+library instead, ``bit_integer_gemm_amd/ab/liblbgemm_NAME.so``, with one design
+choice turned off (see AB_BUILDS); ``bench.py --lib`` loads it.  The library the
+package uses is never built that way.
 """
 from __future__ import annotations
 
@@ -29,6 +34,16 @@ FLAGS = [
     "-Wall", "-Werror", "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
+
+
+# A/B profiling builds: one design choice of the kernels turned off each
+# (the macros are documented in csrc/lb_mfma.hip and csrc/lb_device.hpp).
+AB_BUILDS = {
+    "no_swizzle": ["-DLB_AB_LDS_SWIZZLE=0"],
+    "rows_spread": ["-DLB_AB_COPY_ROWS_SPREAD=1"],
+    "plain_tile_map": ["-DLB_AB_TILE_MAP_PLAIN=1"],
+}
+AB_DIR = os.path.join(PKG, "ab")
 
 
 def sources():
@@ -80,34 +95,46 @@ def ensure_built(verbose: bool = False) -> str:
     return LIB
 
 
-def _compile(src: str, sha: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, f'-DLB_SOURCE_SHA="{sha}"', "-x", "hip", "-c", src, "-o", obj]
+def _compile(src: str, sha: str, objdir: str = OBJDIR, defines=()) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, f'-DLB_SOURCE_SHA="{sha}"', *defines, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, ab: str = None) -> str:
+    lib, objdir, defines = LIB, OBJDIR, ()
+    if ab is not None:
+        if ab not in AB_BUILDS:
+            raise ValueError(f"unknown A/B build {ab!r}; choose from {sorted(AB_BUILDS)}")
+        lib = os.path.join(AB_DIR, f"liblbgemm_{ab}.so")
+        objdir = os.path.join(OBJDIR, "ab_" + ab)
+        defines = tuple(AB_BUILDS[ab])
+        os.makedirs(AB_DIR, exist_ok=True)
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     sha = source_sha()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda f: _compile(f, sha), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, sha, objdir, defines), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
-    os.replace(tmp, LIB)
-    if built_sha() != sha:
-        raise RuntimeError(f"{LIB} does not carry the source hash {sha}")
+    os.replace(tmp, lib)
+    if built_sha(lib) != sha:
+        raise RuntimeError(f"{lib} does not carry the source hash {sha}")
     if verbose:
-        print(f"built {LIB} (sources {sha})")
-    return LIB
+        print(f"built {lib} (sources {sha}{', A/B ' + ab if ab else ''})")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--ab", choices=sorted(AB_BUILDS), help="build an A/B profiling library instead")
+    a = ap.parse_args()
+    build(verbose=True, ab=a.ab)
     sys.exit(0)

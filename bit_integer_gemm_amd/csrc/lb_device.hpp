@@ -101,9 +101,19 @@ __device__ inline uint32_t lds_addr(const void *p)
 // all XCDs read at the same time through the shared last-level cache; it was
 // chosen per tile size from measurements (4 for the medium and large tiles, 8
 // for the small one).
+// (LB_AB_TILE_MAP_PLAIN=1, set only by A/B profiling builds: plain row-major
+// tile order instead.)
+#ifndef LB_AB_TILE_MAP_PLAIN
+#define LB_AB_TILE_MAP_PLAIN 0
+#endif
 __device__ inline void tile_of_block(uint32_t bid, uint32_t tiles_m, uint32_t tiles_n,
                                      uint32_t group, uint32_t &tm, uint32_t &tn)
 {
+    if (LB_AB_TILE_MAP_PLAIN) {
+        tm = bid / tiles_n;
+        tn = bid % tiles_n;
+        return;
+    }
     const uint32_t T = tiles_m * tiles_n;
     const uint32_t q = T / 8u, r = T % 8u;
     const uint32_t xcd = bid % 8u, idx = bid / 8u;

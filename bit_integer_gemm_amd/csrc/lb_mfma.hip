@@ -87,14 +87,41 @@ struct MfmaCfg {
     static_assert(ST * STAGE_BYTES <= 160 * 1024, "LDS");
 };
 
+// Design choices that profiling builds can turn off, one at a time, for A/B
+// measurements (the library is always built with the defaults; the package's
+// build tool makes the A/B libraries, see its --ab option):
+//   LB_AB_LDS_SWIZZLE=0     no XOR permutation of 16-byte chunks in LDS
+//                           (fragment reads then collide on LDS banks)
+//   LB_AB_COPY_ROWS_SPREAD=1 in the 16-row blocks, consecutive copy lanes take
+//                           16 different rows instead of 4 lanes per row
+//   LB_AB_TILE_MAP_PLAIN=1  workgroups take tiles in row-major order (no XCD
+//                           runs, no bands)
+// Each keeps the results exact; only the speed changes.
+#ifndef LB_AB_LDS_SWIZZLE
+#define LB_AB_LDS_SWIZZLE 1
+#endif
+#ifndef LB_AB_COPY_ROWS_SPREAD
+#define LB_AB_COPY_ROWS_SPREAD 0
+#endif
+
 // Layout of a 16-row x 64-byte block: row r's chunk c sits at 16-byte slot
 // 4*r + (c ^ ((r >> 1) & 3)).  A copy lane i fills slot i, i.e. row i/4.
-__device__ inline uint32_t blk_row_of_lane(uint32_t lane) { return lane >> 2; }
-__device__ inline uint32_t blk_chunk_of_lane(uint32_t lane) { return (lane & 3u) ^ ((lane >> 3) & 3u); }
+// (A/B build with spread copies: slot 16*c + r, lane i takes row i%16, chunk
+// i/16, and the fragment read of lane l is slot l.)
+__device__ inline uint32_t blk_row_of_lane(uint32_t lane)
+{
+    return LB_AB_COPY_ROWS_SPREAD ? lane & 15u : lane >> 2;
+}
+__device__ inline uint32_t blk_chunk_of_lane(uint32_t lane)
+{
+    if (LB_AB_COPY_ROWS_SPREAD) return lane >> 4;
+    return LB_AB_LDS_SWIZZLE ? (lane & 3u) ^ ((lane >> 3) & 3u) : lane & 3u;
+}
 __device__ inline uint32_t frag_offset(uint32_t lane)
 {
+    if (LB_AB_COPY_ROWS_SPREAD) return lane * 16u;
     const uint32_t r = lane & 15u, c = lane >> 4;
-    return (4u * r + (c ^ ((r >> 1) & 3u))) * 16u;
+    return (4u * r + (LB_AB_LDS_SWIZZLE ? c ^ ((r >> 1) & 3u) : c)) * 16u;
 }
 
 // Out-of-range K pieces of A in the last (partial) stage are zeroed in LDS:
@@ -583,11 +610,14 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
 //    accumulators between register files.  Its operands come straight from
 //    LDS reads (the compiler waits for them); the accumulators are read only
 //    after 32 wait states past the last MFMA.
-__device__ inline uint32_t wide_chunk_of_lane(uint32_t lane) { return (lane & 7u) ^ (lane >> 3); }
+__device__ inline uint32_t wide_chunk_of_lane(uint32_t lane)
+{
+    return LB_AB_LDS_SWIZZLE ? (lane & 7u) ^ (lane >> 3) : lane & 7u;
+}
 __device__ inline uint32_t wide_frag_offset(uint32_t lane, uint32_t h)
 {
     const uint32_t r = lane & 15u, c = (lane >> 4) + 4u * h;
-    return (r >> 3) * 1024u + (r & 7u) * 128u + 16u * (c ^ (r & 7u));
+    return (r >> 3) * 1024u + (r & 7u) * 128u + 16u * (LB_AB_LDS_SWIZZLE ? c ^ (r & 7u) : c);
 }
 __device__ inline void mfma_tied(i32x4 &c, i32x4 a, i32x4 b)
 {

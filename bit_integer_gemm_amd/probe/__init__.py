@@ -7,7 +7,10 @@ int8 bytes; random e3m2 codes; one bit plane per FP4 nibble, as the 1-bit GEMM
 feeds it).  These rates decide which matrix instruction a low-bit operand is
 worth converting to.
 
-2. Output-store bandwidth when all workgroups store at once, when only one
+2. MFMA throughput with independent vector instructions between the MFMAs
+(does the vector ALU run beside the matrix core, or take its issue slots?).
+
+3. Output-store bandwidth when all workgroups store at once, when only one
 XCD's do, and when one in eight of every XCD's do (256 KiB each, the int32
 tile of a 256 x 256 GEMM tile), to tell a per-XCD limit from a chip-wide one.
 
@@ -50,8 +53,9 @@ def measure(target_ms: float = 8.0) -> dict:
         for wps in (1, 2, 4):
             blocks = cu * wps          # 4 waves per workgroup = one per SIMD
             buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-            iters = 64
-            ms = lib.mfma_rate_run(kind, blocks, iters, ctypes.c_void_p(buf.data_ptr()))
+            iters = 256
+            for _ in range(2):     # the first launch also loads the code object
+                ms = lib.mfma_rate_run(kind, blocks, iters, ctypes.c_void_p(buf.data_ptr()))
             if ms < 0:
                 raise RuntimeError(f"probe launch failed ({ms})")
             iters = max(64, int(iters * target_ms / max(ms, 1e-3)))
@@ -64,6 +68,32 @@ def measure(target_ms: float = 8.0) -> dict:
                 "iters": iters, "ms": round(best, 3)}
             print(f"[probe] {name} waves/SIMD {wps}: {best * 1e6 / n_inst:.2f} ns per instruction per SIMD",
                   flush=True)
+    return out
+
+
+def measure_mix(target_ms: float = 8.0) -> dict:
+    """ns per int8 MFMA per SIMD with V = 0..4 independent VALU instructions
+    after each, at 1 and 2 waves per SIMD."""
+    import torch
+    lib = ctypes.CDLL(LIB)
+    lib.mix_rate_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.mix_rate_run.restype = ctypes.c_float
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {}
+    for wps in (1, 2):
+        blocks = cu * wps
+        buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        for v in range(5):
+            iters = 256
+            for _ in range(2):
+                ms = lib.mix_rate_run(v, blocks, iters, ctypes.c_void_p(buf.data_ptr()))
+            if ms < 0:
+                raise RuntimeError(f"mix probe failed ({ms})")
+            iters = max(64, int(iters * target_ms / max(ms, 1e-3)))
+            best = min(lib.mix_rate_run(v, blocks, iters, ctypes.c_void_p(buf.data_ptr())) for _ in range(3))
+            ns = best * 1e6 / (iters * 16 * wps)
+            out[f"waves_per_simd={wps}/valu_per_mfma={v}"] = {"ns_per_mfma_per_simd": round(ns, 3)}
+            print(f"[probe] mix: {wps} wave(s)/SIMD, {v} VALU per MFMA: {ns:.2f} ns per MFMA per SIMD", flush=True)
     return out
 
 
@@ -93,4 +123,4 @@ def measure_stores(chunk_bytes: int = 256 << 10, reps: int = 5) -> dict:
 def main():
     if not os.path.exists(LIB):
         sys.exit(f"{LIB} not built: run __graft_entry__.build() or bit_integer_gemm_amd.probe.build()")
-    print(json.dumps({"mfma": measure(), "stores": measure_stores()}))
+    print(json.dumps({"mfma": measure(), "mix": measure_mix(), "stores": measure_stores()}))

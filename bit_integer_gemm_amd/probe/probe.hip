@@ -13,6 +13,8 @@
 // (all of them; those of one XCD; or 1 in 8 of every XCD's).  Whether the
 // store phase of a GEMM is bound per XCD or chip-wide decides whether
 // staggering tiles in time can hide it.
+//
+// 3. (below) MFMA throughput with independent vector instructions between.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,6 +97,37 @@ __global__ __launch_bounds__(256) void rate_kernel(uint32_t seed, int iters, flo
     out[gid] = total;
 }
 
+// 3. Matrix core and vector ALU side by side: every int8 16x16x64 MFMA is
+// followed by V independent vector instructions (v_xor_b32 on registers no
+// MFMA reads).  If the two share one issue slot per SIMD, time per MFMA grows
+// by the VALU issue time (4 cycles for a wave64 instruction on 16 lanes) as
+// soon as V is large enough; if they run side by side, it stays flat while
+// the vector work fits in the MFMA's own duration.
+template <int V>
+__global__ __launch_bounds__(256) void mix_kernel(uint32_t seed, int iters, float *out)
+{
+    const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+    const i32x4 a = {(int)mix(seed ^ gid), (int)mix(seed + gid), (int)mix(seed * 3u + gid), (int)mix(gid)};
+    const i32x4 b = {(int)mix(a[0]), (int)mix(a[1]), (int)mix(a[2]), (int)mix(a[3])};
+    i32x4 acc[16];
+    for (int q = 0; q < 16; ++q) acc[q] = i32x4{0, 0, 0, 0};
+    uint32_t x0 = gid, x1 = gid * 7u, x2 = gid * 13u, x3 = gid * 29u;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc[q]) : "v"(a), "v"(b));
+            if constexpr (V >= 1) asm volatile("v_xor_b32 %0, 0x55, %0" : "+v"(x0));
+            if constexpr (V >= 2) asm volatile("v_xor_b32 %0, 0x55, %0" : "+v"(x1));
+            if constexpr (V >= 3) asm volatile("v_xor_b32 %0, 0x55, %0" : "+v"(x2));
+            if constexpr (V >= 4) asm volatile("v_xor_b32 %0, 0x55, %0" : "+v"(x3));
+        }
+    }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    float total = (float)(x0 ^ x1 ^ x2 ^ x3);
+    for (int q = 0; q < 16; ++q) total += (float)(acc[q][0] + acc[q][1] + acc[q][2] + acc[q][3]);
+    out[gid] = total;
+}
+
 // Workgroup b writes bytes [b * chunk, (b + 1) * chunk) of out when it is
 // selected: mode 0 every workgroup, mode 1 those with b % 8 == 0 (consecutive
 // workgroups go round robin over the 8 XCDs, so: the CUs of one XCD), mode 2
@@ -110,6 +143,30 @@ __global__ __launch_bounds__(256) void store_kernel(i32x4 *out, int chunk_vec, i
 }
 
 extern "C" {
+
+// Launch `blocks` workgroups of mix_kernel<v_per_mfma> (0..4); out holds
+// blocks * 256 floats.  Milliseconds between HIP events, or < 0 on error.
+float mix_rate_run(int v_per_mfma, int blocks, int iters, float *out)
+{
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1.f;
+    (void)hipEventRecord(e0, 0);
+    switch (v_per_mfma) {
+    case 0: hipLaunchKernelGGL(mix_kernel<0>, dim3(blocks), dim3(256), 0, 0, 99u, iters, out); break;
+    case 1: hipLaunchKernelGGL(mix_kernel<1>, dim3(blocks), dim3(256), 0, 0, 99u, iters, out); break;
+    case 2: hipLaunchKernelGGL(mix_kernel<2>, dim3(blocks), dim3(256), 0, 0, 99u, iters, out); break;
+    case 3: hipLaunchKernelGGL(mix_kernel<3>, dim3(blocks), dim3(256), 0, 0, 99u, iters, out); break;
+    case 4: hipLaunchKernelGGL(mix_kernel<4>, dim3(blocks), dim3(256), 0, 0, 99u, iters, out); break;
+    default: return -2.f;
+    }
+    (void)hipEventRecord(e1, 0);
+    if (hipEventSynchronize(e1) != hipSuccess) return -3.f;
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return hipGetLastError() == hipSuccess ? ms : -4.f;
+}
 
 // Launch `blocks` workgroups of store_kernel writing `chunk_bytes` each (a
 // multiple of 16) into out, which must hold blocks * chunk_bytes bytes.
