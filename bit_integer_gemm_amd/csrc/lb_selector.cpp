@@ -4,13 +4,14 @@
 // GEMM Optimization via Neural Networks" recasts tuning as classification:
 // time the nine tile x stage templates over many (M, N, K) on a GPU, label
 // each shape with its fastest template (Research results, item 2), and at run
-// time predict the label from M, N, K and the multiprocessor count, scoring a
-// prediction right when the true best is among the top two (item 3).  Here
-// the labels come from timings measured on MI355X and compiled in as a table
-// (selector_table.inc, written by the package's sweep tool); a query takes the
-// label of the nearest measured shape in log2 space.  Shapes of a dtype with
-// no measurements get the default variant.  With LB_SELECTOR=mlp in the
-// environment the pages' feed-forward classifier decides instead.
+// time predict the template from M, N, K and the multiprocessor count with a
+// small feed-forward network, scoring a prediction right when the true best
+// is among the top two (item 3).  Here the network (selector_mlp.inc, trained
+// offline on timings measured on MI355X) decides by default; a shape that
+// the sweep measured exactly takes its measured label.  With LB_SELECTOR=table
+// the label of the nearest measured shape in log2 space decides instead
+// (selector_table.inc, written by the package's sweep tool).  Shapes of a
+// dtype with no measurements get the default variant.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -114,7 +115,8 @@ void mlp_scores(int dtype, int64_t M, int64_t N, int64_t K, int cu, float *score
 }
 
 // The network decides unless LB_SELECTOR=table asks for the table of measured
-// labels (or the dtype has no trained network).
+// labels (or the dtype has no trained network); in network mode a shape that
+// the table holds exactly still takes its measured label.
 bool use_mlp(int dtype)
 {
     const char *e = std::getenv("LB_SELECTOR");
@@ -184,6 +186,24 @@ void table_choice(int dtype, int64_t M, int64_t N, int64_t K, int *best, int *se
     *second = pts[bi].second;
 }
 
+// The measured label when (M, N, K) is itself a shape of the table (a shape
+// the sweep timed), else -1.
+int measured_label(int dtype, int64_t M, int64_t N, int64_t K, int *second)
+{
+    if ((M & (M - 1)) != 0 || (N & (N - 1)) != 0) return -1;
+    int lm = 0, ln = 0;
+    while ((int64_t)1 << lm < M) ++lm;
+    while ((int64_t)1 << ln < N) ++ln;
+    for (int i = 0; i < kTableLen; ++i) {
+        const SelEntry &e = kTable[i];
+        if (e.dtype == dtype && e.log2m == lm && e.log2n == ln && e.k == K) {
+            *second = e.second;
+            return e.best;
+        }
+    }
+    return -1;
+}
+
 // Lowest predicted regret, then the second lowest (ties to the lower index).
 void mlp_choice(int dtype, int64_t M, int64_t N, int64_t K, int cu, int *best, int *second)
 {
@@ -227,9 +247,15 @@ int select_from_table(int dtype, int64_t M, int64_t N, int64_t K, int cu_count, 
     CacheSlot &c = t_cache[(h >> 32) & 15u];
     if (!(c.valid && c.M == M && c.N == N && c.K == K && c.dtype == dtype && c.cu == cu_count &&
           c.mode == mode)) {
-        int b = 0, s2 = 0;
-        if (mode) mlp_choice(dtype, M, N, K, cu_count, &b, &s2);
-        else table_choice(dtype, M, N, K, &b, &s2);
+        int b = -1, s2 = 0;
+        // A shape the sweep measured (on a GPU of the table's 256 CUs) takes
+        // its measured label in either mode; any other shape the mode's
+        // prediction.
+        if (mode && cu_count == 256) b = measured_label(dtype, M, N, K, &s2);
+        if (b < 0) {
+            if (mode) mlp_choice(dtype, M, N, K, cu_count, &b, &s2);
+            else table_choice(dtype, M, N, K, &b, &s2);
+        }
         c = {M, N, K, dtype, cu_count, mode, b, s2, true};
     }
     *best = c.best;

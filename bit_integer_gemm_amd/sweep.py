@@ -498,8 +498,11 @@ def score_heldout(paths, eps=EPS, default=DEFAULT, query_library=True):
             "speedup_vs_best_fixed": {"geomean": gm([r["sec"][fixed] / ts for r, ts in zip(rows, t_sel)]),
                                       "min": min(r["sec"][fixed] / ts for r, ts in zip(rows, t_sel))},
         }
+    out["all_variants_agree"] = all(r["agree"] for r in rows)
+    if any(r.get("auto_sec") is None for r in rows):
+        return out
     # the automatic path (recorded with the library the timings were taken
-    # with: its choice, plus any two-launch split, K bands or stream-K)
+    # with: its choice, plus any two-launch split or K bands)
     sp = [r["sec"][default] / r["auto_sec"] for r in rows]
     sp_sel = [r["sec"][r["network"][0]] / r["auto_sec"] for r in rows]
     out["automatic_path"] = {
@@ -507,7 +510,6 @@ def score_heldout(paths, eps=EPS, default=DEFAULT, query_library=True):
         "speedup_vs_selected_variant": {"geomean": gm(sp_sel), "min": min(sp_sel), "max": max(sp_sel)},
         "slower_than_default": [(r["M"], r["N"], r["K"], round(x, 3)) for r, x in zip(rows, sp)
                                 if x < 1 / (1 + eps)]}
-    out["all_variants_agree"] = all(r["agree"] for r in rows)
     return out
 
 

@@ -59,6 +59,18 @@ def test_measured_shapes_map_to_their_labels(table_mode):
         assert lb.lb_select_variant(d, 2 ** lm, 2 ** ln, k, 256) == (b, s)
 
 
+def test_measured_shapes_keep_their_labels_in_network_mode():
+    """A shape the sweep measured takes its measured label in the default
+    (network) mode as well, on a GPU with the table's 256 CUs; with another CU
+    count the network decides."""
+    ents = table_entries()
+    for d, lm, ln, k, b, s in ents:
+        assert lb.lb_select_variant(d, 2 ** lm, 2 ** ln, k, 256) == (b, s)
+    nets = selector_mlp.read_inc()
+    d, lm, ln, k, b, s = ents[len(ents) // 2]
+    assert lb.lb_select_variant(d, 2 ** lm, 2 ** ln, k, 304) == selector_mlp.choose(nets[d], 2 ** lm, 2 ** ln, k, 304)
+
+
 def test_off_grid_shapes_take_nearest_label(table_mode):
     ents = table_entries()
     g = np.random.Generator(np.random.PCG64(5))
