@@ -231,14 +231,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     // (medium and large tiles; the small tile keeps its five workgroups per CU
     // and reads the scales from global memory).
     constexpr bool LDS_SCALES = KIND == KIND_LINEAR && C::BM >= 128;
-    // int4 2-stage large tile: the next stage's copies go out one or a few at
-    // a time between the first K block's MFMAs instead of in one burst after
-    // the barrier.  With 8 waves of 64x128 this ran 2-7% faster than the
-    // 16-wave tile with burst copies on every shape timed (4096^3: 59.9 against
-    // 61.6 us; 8192 x 8192 x 4096: 227.9 against 243.8 us); either change alone
-    // was mixed.
-    constexpr bool SPREAD = KIND == KIND_S4 && C::BM == 256 && C::ST == 2 && !CONV;
-    constexpr bool LATE_COPIES = (C::NW == 4 || KIND == KIND_S4) && !SPREAD;
+    constexpr bool LATE_COPIES = C::NW == 4 || KIND == KIND_S4;
     constexpr int SCALE_BYTES = LDS_SCALES ? (C::BM + C::BN) * 4 : 0;
     __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE_BYTES + SCALE_BYTES];
 
@@ -352,13 +345,6 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
         }
     };
 
-    // One copy (index i of this wave's NDMA) of a stage into a slot.
-    auto issue_q = [&](const i32x4 &ra, const i32x4 &rb, int slot, int i) {
-        const bool isA = i < C::NDMA_A;
-        const int j = (int)wave + C::NW * (isA ? i : i - C::NDMA_A);
-        dma16(isA ? ra : rb, voff[i], smem_base + slot * C::STAGE_BYTES + (isA ? j : C::ABLK + j) * 1024);
-    };
-
     using Acc = std::conditional_t<KIND == KIND_B1F4, f32x4, i32x4>;
     Acc acc[C::FM][C::FN];
 #pragma unroll
@@ -419,7 +405,7 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
             // 1-bit tiles, 5% slower for the small tile.  The 16-wave int4 tile
             // copies first: holding its fragments over the copies would spill.
             if (kb == 0) {
-                if constexpr (!LATE_COPIES && !SPREAD) {
+                if constexpr (!LATE_COPIES) {
                     if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1, (int)((kt + C::ST - 1) % C::ST));
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -431,38 +417,15 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                     alo[i] = s4_even_plane(af[i]);
                     ahi[i] = af[i] & (int)0xF0F0F0F0;
                 }
-                i32x4 sra = i32x4{0, 0, 0, 0}, srb = i32x4{0, 0, 0, 0};
-                const bool scp = SPREAD && kb == 0 && kt + C::ST - 1 < nk;
-                if constexpr (SPREAD) {
-                    if (scp) {
-                        const int64_t k0 = (kt + C::ST - 1) * C::BK;
-                        sra = make_rsrc(Ab + k0, a_bytes > k0 ? (uint64_t)(a_bytes - k0) : 0);
-                        srb = make_rsrc(Bb + k0, b_bytes > k0 ? (uint64_t)(b_bytes - k0) : 0);
-                    }
-                }
 #pragma unroll
                 for (int j = 0; j < C::FN; ++j) {
-                    if constexpr (SPREAD) {
-                        if (scp) {
-#pragma unroll
-                            for (int q = j * C::NDMA / C::FN; q < (j + 1) * C::NDMA / C::FN; ++q)
-                                issue_q(sra, srb, (int)((kt + C::ST - 1) % C::ST), q);
-                        }
-                    }
                     const i32x4 blo = s4_even_plane(bf[j]);
                     const i32x4 bhi = bf[j] & (int)0xF0F0F0F0;
-                    // In the spread-copy tile two waves share each SIMD; the one
-                    // entering its MFMA run is issued first, the other's unpack
-                    // and copies fill in behind it (measured 0.7-1% faster at
-                    // 4096^3, 8192 x 8192 x 4096 and 4096 x 4096 x 8192; the
-                    // other int4 tiles lost up to 3% with it and run without).
-                    if constexpr (SPREAD) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                     for (int i = 0; i < C::FM; ++i) {
                         acc[i][j] = mfma16(blo, alo[i], acc[i][j]);
                         acc[i][j] = mfma16(bhi, ahi[i], acc[i][j]);
                     }
-                    if constexpr (SPREAD) __builtin_amdgcn_s_setprio(0);
                 }
             } else if constexpr (KIND == KIND_B1) {
                 // Bit 7 of every byte first, from the words as loaded: A's as
@@ -579,12 +542,12 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     }
 }
 
-// ---- large int8 tile on four waves --------------------------------------
-// The 2-stage large variant of the int8 GEMM and the int8 linear layer: a
-// 256x256 tile on four waves (one per SIMD) of 128x128, all 256 int32
+// ---- large tile on four waves (int8, int4, int8 linear) -----------------
+// The 2-stage large variant of the int8 and int4 GEMMs and the int8 linear
+// layer: a 256x256 tile on four waves (one per SIMD) of 128x128, all 256 int32
 // accumulators of a lane in AGPRs.  Per workgroup, per 64 K-bytes: 64 KiB of
-// LDS fragment reads for 256 MFMAs, against 128 KiB for sixteen waves of
-// 64x64.
+// LDS fragment reads for 256 MFMAs (512 for int4), against 128 KiB for
+// sixteen waves of 64x64.
 //  * Two LDS super-stages of 128 K-bytes (64 KiB each: 256 A rows, 256 B rows)
 //    form the 2-stage ring.  A 2 KiB block holds 16 rows x 128 bytes as two
 //    1 KiB halves of 8 rows; row r's 16-byte chunk c sits at
@@ -595,16 +558,30 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
 //    r..r+7 of one half, at distinct slots (c + 4h) ^ (r%8).
 //  * Block t (64 K-bytes) is half t%2 of super-stage t/2.  Each block runs
 //    its MFMAs in two halves (rows 0-3, then 4-7 of the wave's 8x8 fragment
-//    grid); the next block's 16 fragments are read between the second half's
-//    MFMAs, so LDS latency stays under the matrix cores.  After the first
-//    half of an odd block every wave is done with that block's super-stage:
-//    wait for the next super-stage's copies, barrier, and refill the free slot
-//    with the super-stage after next (the pipeline of Research results item
-//    1, two stages deep).
-//  * The refill's 16 copies per wave go out one per two MFMAs of the second
-//    half.  Issued in one burst, a wave that alone feeds its SIMD stalls on
-//    the full copy queue: 62.1 against 59.6 us at int8 4096^3 (the 16-wave
-//    kernel: 63.8 us).
+//    grid); the next block's 16 fragments (B first: the next block's first
+//    row needs all of them) are read between the second half's MFMAs, so LDS
+//    latency stays under the matrix cores.  After the first half of an odd
+//    block every wave is done with that block's super-stage: wait for the
+//    next super-stage's copies, barrier, and refill the free slot with the
+//    super-stage after next (the pipeline of Research results item 1, two
+//    stages deep).
+//  * The refill's 16 copies per wave go out one per four MFMA slots: copies
+//    0-7 between the second half's MFMAs, 8-15 between those of the next
+//    (even) block's first half, which still leaves one block of MFMAs before
+//    the wait.  A copy costs its wave about 11-14 cycles next to the MFMAs, but
+//    a CU's copy path moves 64 bytes per cycle: the earlier schedule, four
+//    waves each issuing 16 copies within 32 MFMAs, saturated it and stalled
+//    every wave (cycle counts at int8 4096^3: 97.0k loop cycles per wave
+//    against 70.3k for the MFMAs alone; spread, 87.6k).  When no super-stage
+//    is left to load, the copies read an empty buffer range (zeros, no memory
+//    traffic) into the slot just released, which nothing reads again, so the
+//    copy code has no branches (a branch per copy cost several percent).
+//  * int4: the LDS holds packed bytes and each fragment is unpacked in
+//    registers into its even-k and odd-k planes (see s4_even_plane), two
+//    MFMAs per fragment pair.  A row's two A planes are made before its
+//    MFMAs; B's planes are made for the whole block in its first row.  One
+//    wave per SIMD issues its unpack next to its own MFMAs, and every copy
+//    now serves twice the MFMAs of the int8 tile.
 //  * The MFMA is inline assembly with the accumulator tied to its AGPR: with
 //    the builtin the compiler picks the untied form and shuffles all 256
 //    accumulators between register files.  Its operands come straight from
@@ -728,6 +705,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     const uint32_t foff0 = wide_frag_offset(lane, 0), foff1 = wide_frag_offset(lane, 1);
     auto fptr = [&](int t) { return smem + ((t / 2) % 2) * SS + ((t % 2) ? foff1 : foff0); };
+    // int4: the offsets are remade per block from the lane (a few vector
+    // instructions) rather than held across the loop in two registers.
+    auto fptr4 = [&](int t) {
+        uint32_t l = lane;
+        asm volatile("" : "+v"(l));
+        return smem + ((t / 2) % 2) * SS + wide_frag_offset(l, (uint32_t)(t % 2));
+    };
 
     i32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
     {
@@ -738,56 +722,195 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int j = 0; j < FN; ++j) fb0[j] = *(const i32x4 *)(f + 32768 + (wn * FN + j) * 2048);
     }
 
-    // Refill state of the current odd block: copies of super-stage cp_ss, if any.
-    i32x4 cra = i32x4{0, 0, 0, 0}, crb = i32x4{0, 0, 0, 0};
-    uint32_t csb = 0;
-    bool cp = false;
+    // Refill of the slot released at the last odd block's barrier (no refill
+    // due: an empty buffer range, read into that slot).  Before the first
+    // barrier there is none, and the first block issues no copies.
+    const i32x4 none = make_rsrc(A, 0);
+    i32x4 cra = none, crb = none;
+    uint32_t csb = smem_base;
+    auto copy_r = [&](int q) { copy_q(cra, crb, csb, q); };
 
-    // MFMAs of fragment rows i0 .. i0+3; the second half also reads the next
-    // block's fragments from f and issues the refill copies.
-    auto half = [&](const i32x4 *fa, const i32x4 *fb, int i0, bool second, const char *f,
+    // MFMAs of fragment rows i0 .. i0+3 (int8).  CP: issue refill copies
+    // (eight, two per row): copies 8-15 in an even block's first half, 0-7 in
+    // an odd block's second half.  The second half also reads the next
+    // block's fragments from f, four per row.
+    auto half = [&](auto cp_c, const i32x4 *fa, const i32x4 *fb, int i0, bool second, const char *f,
                     i32x4 *na, i32x4 *nb) {
+        constexpr bool CP = decltype(cp_c)::value;
 #pragma unroll
         for (int i = i0; i < i0 + FM / 2; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 mfma_tied(acc[i][j], fb[j], fa[i]);
-                if (second) {
+                if (CP && j % 4 == 0) copy_r((second ? 0 : 8) + (i - i0) * 2 + j / 4);
+                if (second && j % 2 == 1) {
                     const int q = (i - i0) * 4 + j / 2;  // 0..15
-                    if (j % 2 == 0 && cp) copy_q(cra, crb, csb, q);
-                    if (j % 2 == 1) {
-                        if (q < FM) na[q] = *(const i32x4 *)(f + (wm * FM + q) * 2048);
-                        else nb[q - FM] = *(const i32x4 *)(f + 32768 + (wn * FN + q - FM) * 2048);
-                    }
+                    if (q < FN) nb[q] = *(const i32x4 *)(f + 32768 + (wn * FN + q) * 2048);
+                    else na[q - FN] = *(const i32x4 *)(f + (wm * FM + q - FN) * 2048);
                 }
             }
     };
-    auto body = [&](int t, const i32x4 *ca, const i32x4 *cb, i32x4 *na, i32x4 *nb) {
-        half(ca, cb, 0, false, nullptr, na, nb);
-        if (t % 2 == 1) {
+    // One 64-byte K block; PAR = t % 2, FIRST: block 0 (no refill pending).
+    auto body = [&](auto par_c, auto first_c, int t, const i32x4 *ca, const i32x4 *cb, i32x4 *na,
+                    i32x4 *nb) {
+        constexpr int PAR = decltype(par_c)::value;
+        constexpr bool FIRST = decltype(first_c)::value;
+        half(std::integral_constant<bool, PAR == 0 && !FIRST>{}, ca, cb, 0, false, nullptr, na, nb);
+        if constexpr (PAR == 1) {
             wait_vm_barrier<0>();
             const int ss = t / 2;
-            cp = ss + 2 < nss;
-            if (cp) {
-                cra = rsrc_a(ss + 2);
-                crb = rsrc_b(ss + 2);
-                csb = smem_base + (uint32_t)((ss % 2) * SS);
-            }
+            const bool more = ss + 2 < nss;
+            cra = more ? rsrc_a(ss + 2) : none;
+            crb = more ? rsrc_b(ss + 2) : none;
+            csb = smem_base + (uint32_t)((ss % 2) * SS);
             if (k_tail && ss + 1 == nss - 1) {
                 zero_tail((ss + 1) % 2, (int64_t)(nss - 1) * 128);
                 barrier_lds();
             }
         }
         // After the last block the reads fetch stale LDS that nothing uses.
-        half(ca, cb, FM / 2, true, fptr(t + 1), na, nb);
-        cp = false;
+        half(std::integral_constant<bool, PAR == 1>{}, ca, cb, FM / 2, true, fptr(t + 1), na, nb);
     };
-    int t = 0;
-    for (; t + 1 < nk; t += 2) {
-        body(t, fa0, fb0, fa1, fb1);
-        body(t + 1, fa1, fb1, fa0, fb0);
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using F0 = std::false_type;
+    if constexpr (KIND != KIND_S4) {
+        body(P0{}, std::true_type{}, 0, fa0, fb0, fa1, fb1);
+        int t = 1;
+        for (; t + 1 < nk; t += 2) {
+            body(P1{}, F0{}, t, fa1, fb1, fa0, fb0);
+            body(P0{}, F0{}, t + 1, fa0, fb0, fa1, fb1);
+        }
+        if (t < nk) body(P1{}, F0{}, t, fa1, fb1, fa0, fb0);
+    } else {
+        // int4.  Per block (256 MFMA slots per wave) 160 vector instructions
+        // make the even-k and odd-k planes of 16 fragments.  Next to a wave's
+        // own MFMAs about two vector instructions per MFMA issue free, and
+        // each further one costs about 4 cycles (measured), so they are
+        // placed one by one: each is an asm statement, kept in order with the
+        // MFMAs.  A planes, one register set: the next row's even-k plane is
+        // made in slots 8-13 of a row (after its last even-k MFMA), a row's
+        // odd-k plane in its slots 0-3.  B fragments of the next block: read
+        // in the first eight slots of the second half into the odd-k plane
+        // array and unpacked in place, their 80 instructions spread over the
+        // half's slots 12-63 (at most two per slot); the B planes are double
+        // buffered.  A fragments of the next block: read in the second half
+        // over the ones whose planes are made (single buffer).  Every plane is
+        // complete at least two instructions before its first MFMA (the
+        // hazard the compiler does not check around assembly MFMAs).
+        i32x4 *fa = fa0;
+        i32x4 *bhi4[2] = {fb0, fb1};   // packed B, then its odd-k plane in place
+        i32x4 blo4[2][FN];             // even-k planes of B
+        const int msk = __builtin_amdgcn_readfirstlane((int)0xF0F0F0F0);
+        auto shl4 = [](int lo, int hi) {
+            uint64_t x = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+            asm volatile("v_lshlrev_b64 %0, 4, %1" : "=v"(x) : "v"(x));
+            return x;
+        };
+        auto andm = [&](int x) {
+            int r;
+            asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "s"(msk), "v"(x));
+            return r;
+        };
+        // Step k (0..9) of making planes (lo, hi) of packed fragment w: the
+        // 64-bit shifts write lo's register pairs, which are then masked in
+        // place; hi may be w itself (in place).
+        auto plane_op = [&](int k, i32x4 &w, i32x4 &lo, i32x4 &hi) {
+            if (k == 0 || k == 1) {
+                const uint64_t x = shl4(k == 0 ? w.x : w.z, k == 0 ? w.y : w.w);
+                if (k == 0) { lo.x = (int)(uint32_t)x; lo.y = (int)(uint32_t)(x >> 32); }
+                else { lo.z = (int)(uint32_t)x; lo.w = (int)(uint32_t)(x >> 32); }
+            }
+            else if (k == 2) lo.x = andm(lo.x);
+            else if (k == 3) lo.y = andm(lo.y);
+            else if (k == 4) lo.z = andm(lo.z);
+            else if (k == 5) lo.w = andm(lo.w);
+            else if (k == 6) hi.x = andm(w.x);
+            else if (k == 7) hi.y = andm(w.y);
+            else if (k == 8) hi.z = andm(w.z);
+            else hi.w = andm(w.w);
+        };
+        i32x4 alo, ahi;
+        // Refill copies walk their offsets (copy q of a wave reads 32 rows of
+        // K bytes past copy q-1) in one register instead of eight.
+        const uint32_t kstride = (uint32_t)Kb * 32u;
+        uint32_t vcur = voff[0];
+        auto copy_r4 = [&](int q) {
+            if (q % 8 == 0) vcur = voff[0];
+            dma16(q < 8 ? cra : crb, vcur,
+                  csb + (q < 8 ? 0u : 32768u) + ((uint32_t)wave + 4u * (uint32_t)(q % 8)) * 1024u);
+            asm volatile("v_add_u32 %0, %1, %0" : "+v"(vcur) : "s"(kstride));
+        };
+        // Block 0: its B planes and row 0's A planes before the first MFMA.
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int k = 0; k < 10; ++k) plane_op(k, bhi4[0][j], blo4[0][j], bhi4[0][j]);
+#pragma unroll
+        for (int k = 0; k < 10; ++k) plane_op(k, fa[0], alo, ahi);
+        asm volatile("s_nop 1" ::: "memory");
+
+        auto body4 = [&](auto par_c, auto first_c, int t) {
+            constexpr int P = decltype(par_c)::value, Q = 1 - P;
+            constexpr bool FIRST = decltype(first_c)::value;
+            const char *f = fptr4(t + 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const bool second = i >= FM / 2;
+                if (i == FM / 2 && P == 1) {
+                    wait_vm_barrier<0>();
+                    const int ss = t / 2;
+                    const bool more = ss + 2 < nss;
+                    cra = more ? rsrc_a(ss + 2) : none;
+                    crb = more ? rsrc_b(ss + 2) : none;
+                    csb = smem_base + (uint32_t)((ss % 2) * SS);
+                    if (k_tail && ss + 1 == nss - 1) {
+                        zero_tail((ss + 1) % 2, (int64_t)(nss - 1) * 128);
+                        barrier_lds();
+                    }
+                }
+#pragma unroll
+                for (int sl = 0; sl < 2 * FN; ++sl) {
+                    const int j = sl % FN;
+                    const bool odd = sl >= FN;
+                    mfma_tied(acc[i][j], odd ? bhi4[P][j] : blo4[P][j], odd ? ahi : alo);
+                    // refill copies: 8-15 in an even block's first half, 0-7 in an
+                    // odd block's second half, two per row
+                    const bool cp = second ? P == 1 : (P == 0 && !FIRST);
+                    if (cp && sl % FN == 0) copy_r4((second ? 0 : 8) + (i % (FM / 2)) * 2 + sl / FN);
+                    const int z = (i - FM / 2) * 2 * FN + sl;  // slot in the second half
+                    if (second && z < FN) bhi4[Q][z] = *(const i32x4 *)(f + 32768 + (wn * FN + z) * 2048);
+                    // the next block's A fragment q replaces fragment q once
+                    // this block's planes of row q are made: q <= 4 in row 4,
+                    // later ones in their own row, at slots 8-12
+                    if (second && sl >= FN && sl < FN + 5) {
+                        const int q = i == FM / 2 ? sl - FN : (sl == FN ? i : -1);
+                        if (q >= 0) fa[q] = *(const i32x4 *)(f + (wm * FM + q) * 2048);
+                    }
+                    // A planes: the next row's even-k plane into alo after this
+                    // row's last even-k MFMA (slots 8-13; after row FM-1 the next
+                    // block's row 0), this row's odd-k plane into ahi in slots 0-3
+                    // (this row's first odd-k MFMA is at slot 8)
+                    if (sl >= FN && sl < FN + 6) plane_op(sl - FN, fa[(i + 1) % FM], alo, ahi);
+                    if (sl < 4) plane_op(6 + sl, fa[i], alo, ahi);
+                    // the next block's B planes: instruction u at second-half slot 12 + 52u/80
+                    if (second && z >= 12) {
+#pragma unroll
+                        for (int u = 0; u < 10 * FN; ++u)
+                            if (12 + (u * 52) / (10 * FN) == z)
+                                plane_op(u % 10, bhi4[Q][u / 10], blo4[Q][u / 10], bhi4[Q][u / 10]);
+                    }
+                }
+            }
+        };
+        body4(P0{}, std::true_type{}, 0);
+        int t = 1;
+        for (; t + 1 < nk; t += 2) {
+            body4(P1{}, F0{}, t);
+            body4(P0{}, F0{}, t + 1);
+        }
+        if (t < nk) body4(P1{}, F0{}, t);
     }
-    if (t < nk) body(t, fa0, fb0, fa1, fb1);
 
     // The accumulators are read 32 wait states after the last MFMA.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -796,10 +919,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
 
-    // Epilogue: lane holds C[m][n..n+3] of each fragment.
+    // Epilogue: lane holds C[m][n..n+3] of each fragment.  (Kept row by row:
+    // hoisted across rows, the reads of the accumulators that need vector
+    // work first, the int4 shift, crowd the vector registers.)
     const bool vec_ok = ((N | ldo) & 3) == 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
         const int64_t m = m0 + wm * 128 + i * 16 + (lane % 16);
         if (m >= M) continue;
         const float *lds_sx = (const float *)(smem + 2 * SS);
@@ -810,7 +936,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int j = 0; j < FN; ++j) {
             const int64_t n = n0 + wn * 128 + j * 16 + (lane / 16) * 4;
             if (n >= N) continue;
-            const i32x4 v = acc[i][j];
+            i32x4 v = acc[i][j];
+            if constexpr (KIND == KIND_S4) v = v >> 8;
             if constexpr (KIND == KIND_LINEAR) {
                 float *o = (float *)out + m * (int64_t)ldo + n;
                 if (vec_ok) {
@@ -883,8 +1010,8 @@ using M4 = MfmaCfg<128, 128, 64, 2, 2, 4>;    // 64 KiB
 // 16 waves win by 4-9% when there are only 16-64 tiles).  The 1-bit kernels
 // use 8 waves throughout: their per-fragment bit work makes the wider wave
 // tile pay at every depth (124 against 137 us at 4096 x 4096 x 8192 bits with
-// the first bit expansion).  The int4 GEMM's 2-stage tile uses 8 waves too,
-// with its copies spread between MFMAs (see SPREAD in the kernel).
+// the first bit expansion).  The int4 and int8 GEMMs' 2-stage large tile
+// runs on the four-wave kernel (mfma_w4_kernel).
 using L2W16 = MfmaCfg<256, 256, 128, 4, 4, 2>; // 128 KiB
 using L2W8 = MfmaCfg<256, 256, 128, 4, 2, 2>;  // 128 KiB
 using L3W8 = MfmaCfg<256, 256, 64, 4, 2, 3>;   // 96 KiB
@@ -933,10 +1060,10 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     constexpr bool b1 = KIND == KIND_B1 || KIND == KIND_B1F4;
     switch (variant) {
     case 6:
-        // int8 GEMM and linear layer: the four-wave large tile (same 256x256
-        // tile, two stages of 128 K-bytes).  int4 GEMM and 1-bit: 8 waves of
+        // int8 and int4 GEMMs and the linear layer: the four-wave large tile
+        // (same 256x256 tile, two stages of 128 K-bytes).  1-bit: 8 waves of
         // 64x128; the convolution: 16 waves of 64x64.
-        if constexpr ((KIND == KIND_S8 || KIND == KIND_LINEAR) && !CONV)
+        if constexpr ((KIND == KIND_S8 || KIND == KIND_S4 || KIND == KIND_LINEAR) && !CONV)
             return launch_w4<KIND>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
         else
             return launch_one<std::conditional_t<b1 || (KIND == KIND_S4 && !CONV), L2W8, L2W16>, KIND, CONV>(
