@@ -661,6 +661,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     };
 
+    // (1-bit, FP4 route: the accumulators hold fp32 bits, exact counts; a
+    // zero word is 0.0.)
     i32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -771,10 +773,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // After the last block the reads fetch stale LDS that nothing uses.
         half(std::integral_constant<bool, PAR == 1>{}, ca, cb, FM / 2, true, fptr(t + 1), na, nb);
     };
+    // int4 and 1-bit: refill copies walk their offsets (copy q of a wave reads
+    // 32 rows of K bytes past copy q-1) in one register instead of eight.
+    const uint32_t kstride = (uint32_t)Kb * 32u;
+    uint32_t vcur = voff[0];
+    auto copy_r4 = [&](int q) {
+        if (q % 8 == 0) vcur = voff[0];
+        dma16(q < 8 ? cra : crb, vcur,
+              csb + (q < 8 ? 0u : 32768u) + ((uint32_t)wave + 4u * (uint32_t)(q % 8)) * 1024u);
+        asm volatile("v_add_u32 %0, %1, %0" : "+v"(vcur) : "s"(kstride));
+    };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     using F0 = std::false_type;
-    if constexpr (KIND != KIND_S4) {
+    if constexpr (KIND == KIND_S8 || KIND == KIND_LINEAR) {
         body(P0{}, std::true_type{}, 0, fa0, fb0, fa1, fb1);
         int t = 1;
         for (; t + 1 < nk; t += 2) {
@@ -782,7 +794,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             body(P0{}, F0{}, t + 1, fa0, fb0, fa1, fb1);
         }
         if (t < nk) body(P1{}, F0{}, t, fa1, fb1, fa0, fb0);
-    } else {
+    } else if constexpr (KIND == KIND_S4) {
         // int4.  Per block (256 MFMA slots per wave) 160 vector instructions
         // make the even-k and odd-k planes of 16 fragments.  Next to a wave's
         // own MFMAs about two vector instructions per MFMA issue free, and
@@ -831,16 +843,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             else hi.w = andm(w.w);
         };
         i32x4 alo, ahi;
-        // Refill copies walk their offsets (copy q of a wave reads 32 rows of
-        // K bytes past copy q-1) in one register instead of eight.
-        const uint32_t kstride = (uint32_t)Kb * 32u;
-        uint32_t vcur = voff[0];
-        auto copy_r4 = [&](int q) {
-            if (q % 8 == 0) vcur = voff[0];
-            dma16(q < 8 ? cra : crb, vcur,
-                  csb + (q < 8 ? 0u : 32768u) + ((uint32_t)wave + 4u * (uint32_t)(q % 8)) * 1024u);
-            asm volatile("v_add_u32 %0, %1, %0" : "+v"(vcur) : "s"(kstride));
-        };
         // Block 0: its B planes and row 0's A planes before the first MFMA.
 #pragma unroll
         for (int j = 0; j < FN; ++j)
@@ -910,6 +912,131 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             body4(P0{}, F0{}, t + 1);
         }
         if (t < nk) body4(P1{}, F0{}, t);
+    } else {
+        // 1-bit on the FP4 instruction.  A block's 64 K-bytes are 512 bits per
+        // row, four planes of 128 (see fp4_plane): 256 MFMAs per wave, taken
+        // plane by plane (32 rows (plane p, fragment row i) of 8), so that one
+        // plane of B (8 fragments, 32 registers) is live at a time and the
+        // two MFMAs into one accumulator are 64 apart.  The planes are made one
+        // step ahead by single vector instructions placed between the MFMAs
+        // (about two per MFMA issue free next to a wave's own MFMAs): in row
+        // (p, i) the A plane of the next row and B plane p+1 of fragment i.
+        // Packed fragments are single-buffered: in plane 3, once this block's
+        // last planes are made, the next block's B fragments are read in row
+        // (3, 0) and its A fragment i in row (3, i), and the next block's
+        // plane-0 planes are made from them in rows (3, 1..7).  Every plane is
+        // complete at least two instructions before its first MFMA.
+        i32x4 *fa = fa0, *fb = fb0;
+        i32x4 bp[2][FN];   // B planes p (even p) and p+1 (odd p): double buffer
+        i32x4 ap[2];       // A planes of the current and the next row
+        const int m0s = __builtin_amdgcn_readfirstlane(0x11111111), m1s = __builtin_amdgcn_readfirstlane(0x22222222),
+                  m2s = __builtin_amdgcn_readfirstlane(0x44444444);
+        // E8M0 block scales per plane: 2^(1-s), plane 3 2^-1 (its nibbles hold 2.0)
+        int sc0 = 128, sc1 = 127, sc2 = 126;
+        asm volatile("" : "+v"(sc0), "+v"(sc1), "+v"(sc2));
+        auto andm = [](int x, int m) {
+            int r;
+            asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "s"(m), "v"(x));
+            return r;
+        };
+        auto shr1 = [](int lo, int hi) {
+            uint64_t x = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+            asm volatile("v_lshrrev_b64 %0, 1, %1" : "=v"(x) : "v"(x));
+            return x;
+        };
+        auto nops = [](int p) { return p == 3 ? 6 : 4; };
+        // Step k of making plane p of packed fragment w into x.
+        auto plane_op = [&](int p, int k, const i32x4 &w, i32x4 &x) {
+            if (p < 3) {
+                const int m = p == 0 ? m0s : p == 1 ? m1s : m2s;
+                if (k == 0) x.x = andm(w.x, m);
+                else if (k == 1) x.y = andm(w.y, m);
+                else if (k == 2) x.z = andm(w.z, m);
+                else x.w = andm(w.w, m);
+            } else if (k == 0 || k == 1) {
+                const uint64_t v = shr1(k == 0 ? w.x : w.z, k == 0 ? w.y : w.w);
+                if (k == 0) { x.x = (int)(uint32_t)v; x.y = (int)(uint32_t)(v >> 32); }
+                else { x.z = (int)(uint32_t)v; x.w = (int)(uint32_t)(v >> 32); }
+            }
+            else if (k == 2) x.x = andm(x.x, m2s);
+            else if (k == 3) x.y = andm(x.y, m2s);
+            else if (k == 4) x.z = andm(x.z, m2s);
+            else x.w = andm(x.w, m2s);
+        };
+        auto mfma_b1 = [&](i32x4 &c, const i32x4 &b, const i32x4 &a, int s) {
+            asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                         : "+a"(c) : "v"(b), "v"(a), "v"(s));
+        };
+        // Block 0: B plane 0 and row (0, 0)'s A plane before the first MFMA.
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) plane_op(0, k, fb[j], bp[0][j]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) plane_op(0, k, fa[0], ap[0]);
+        asm volatile("s_nop 1" ::: "memory");
+
+        // Half H of a block (planes 2H and 2H+1, 128 MFMAs; unrolled as one
+        // piece the whole block outgrows the compiler's unrolling).
+        auto half1 = [&](auto par_c, auto first_c, auto half_c, int t) {
+            constexpr int P = decltype(par_c)::value, H = decltype(half_c)::value;
+            constexpr bool FIRST = decltype(first_c)::value;
+            const char *f = fptr4(t + 1);
+            if (H == 1 && P == 1) {
+                wait_vm_barrier<0>();
+                const int ss = t / 2;
+                const bool more = ss + 2 < nss;
+                cra = more ? rsrc_a(ss + 2) : none;
+                crb = more ? rsrc_b(ss + 2) : none;
+                csb = smem_base + (uint32_t)((ss % 2) * SS);
+                if (k_tail && ss + 1 == nss - 1) {
+                    zero_tail((ss + 1) % 2, (int64_t)(nss - 1) * 128);
+                    barrier_lds();
+                }
+            }
+#pragma unroll
+            for (int p = 2 * H; p < 2 * H + 2; ++p)
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = p * FM + i;
+                // the next row (after row (3, 7): the next block's row (0, 0))
+                const int pn = (r + 1) / FM % 4, in = (r + 1) % FM;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    mfma_b1(acc[i][j], bp[p % 2][j], ap[r % 2], p == 0 ? sc0 : p == 1 ? sc1 : sc2);
+                    // refill copies: 8-15 in an even block's first half, 0-7 in an
+                    // odd block's second half, one per 16 MFMAs
+                    const bool cp = H == 1 ? P == 1 : (P == 0 && !FIRST);
+                    if (cp && j == 0 && r % 2 == 0) copy_r4((H == 1 ? 0 : 8) + (r % (2 * FM)) / 2);
+                    if (p == 3) {
+                        // plane 3: the next block's fragments
+                        if (i == 0) fb[j] = *(const i32x4 *)(f + 32768 + (wn * FN + j) * 2048);
+                        if (j == 6) fa[i] = *(const i32x4 *)(f + (wm * FM + i) * 2048);
+                    }
+                    // A plane of the next row: slots 1 ..
+                    if (j >= 1 && j - 1 < nops(pn)) plane_op(pn, j - 1, fa[in], ap[(r + 1) % 2]);
+                    // B plane p+1 of fragment i (plane 3: the next block's plane 0
+                    // of fragment i-1, and of fragment 7 too in row (3, 7))
+                    if (p < 3) {
+                        if (j >= 2 && j - 2 < nops(p + 1)) plane_op(p + 1, j - 2, fb[i], bp[(p + 1) % 2][i]);
+                    } else if (i >= 1) {
+                        if (j >= 2 && j < 6) plane_op(0, j - 2, fb[i - 1], bp[0][i - 1]);
+                        if (i == FM - 1 && j >= 4) plane_op(0, j - 4, fb[FM - 1], bp[0][FM - 1]);
+                    }
+                }
+            }
+        };
+        auto body1 = [&](auto par_c, auto first_c, int t) {
+            half1(par_c, first_c, std::integral_constant<int, 0>{}, t);
+            half1(par_c, first_c, std::integral_constant<int, 1>{}, t);
+        };
+        body1(P0{}, std::true_type{}, 0);
+        int t = 1;
+        for (; t + 1 < nk; t += 2) {
+            body1(P1{}, F0{}, t);
+            body1(P0{}, F0{}, t + 1);
+        }
+        if (t < nk) body1(P1{}, F0{}, t);
     }
 
     // The accumulators are read 32 wait states after the last MFMA.
@@ -936,7 +1063,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int j = 0; j < FN; ++j) {
             const int64_t n = n0 + wn * 128 + j * 16 + (lane / 16) * 4;
             if (n >= N) continue;
-            i32x4 v = acc[i][j];
+            i32x4 v;
+            if constexpr (KIND == KIND_B1F4) {
+                // exact: the fp32 sums are integers below 2^24
+                const f32x4 fv = __builtin_bit_cast(f32x4, acc[i][j]);
+                v = i32x4{(int32_t)fv.x, (int32_t)fv.y, (int32_t)fv.z, (int32_t)fv.w};
+            } else
+                v = acc[i][j];
             if constexpr (KIND == KIND_S4) v = v >> 8;
             if constexpr (KIND == KIND_LINEAR) {
                 float *o = (float *)out + m * (int64_t)ldo + n;
@@ -1063,7 +1196,7 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
         // int8 and int4 GEMMs and the linear layer: the four-wave large tile
         // (same 256x256 tile, two stages of 128 K-bytes).  1-bit: 8 waves of
         // 64x128; the convolution: 16 waves of 64x64.
-        if constexpr ((KIND == KIND_S8 || KIND == KIND_S4 || KIND == KIND_LINEAR) && !CONV)
+        if constexpr ((KIND == KIND_S8 || KIND == KIND_S4 || KIND == KIND_LINEAR || KIND == KIND_B1F4) && !CONV)
             return launch_w4<KIND>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
         else
             return launch_one<std::conditional_t<b1 || (KIND == KIND_S4 && !CONV), L2W8, L2W16>, KIND, CONV>(
