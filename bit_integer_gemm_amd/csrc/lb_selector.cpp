@@ -9,12 +9,18 @@
 // is among the top two (item 3).  Here the network (selector_mlp.inc, trained
 // offline on timings measured on MI355X) decides by default; a shape that
 // the sweep measured exactly takes its measured label.  With LB_SELECTOR=table
-// the label of the nearest measured shape in log2 space decides instead
-// (selector_table.inc, written by the package's sweep tool).  Shapes of a
-// dtype with no measurements get the default variant.
+// the measured shapes decide instead: around (M, N, K) the table's grid
+// gives up to eight measured shapes (the grid points bracketing log2 M,
+// log2 N and log2 K), and the variant whose worst time over them, relative to
+// each shape's fastest, is lowest wins (selector_table.inc, written by the
+// package's sweep tool).  On held-out shapes this interpolation beat the
+// label of the single nearest grid shape on geometric-mean and worst-case
+// slowdown for every operand type.  Shapes of a dtype with no measurements get
+// the default variant.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -29,6 +35,7 @@ struct SelEntry {
     int log2m, log2n;
     int k;
     int best, second;
+    uint16_t regret[LB_NUM_VARIANTS];  // time over the fastest, in thousandths
 };
 
 #include "selector_table.inc"
@@ -114,14 +121,15 @@ void mlp_scores(int dtype, int64_t M, int64_t N, int64_t K, int cu, float *score
     dense(W[3], B[3], h1, LB_MLP_HIDDEN, scores, LB_NUM_VARIANTS, false);
 }
 
-// The network decides unless LB_SELECTOR=table asks for the table of measured
-// labels (or the dtype has no trained network); in network mode a shape that
-// the table holds exactly still takes its measured label.
-bool use_mlp(int dtype)
+// Selector mode: 1 (the default) the network, a shape the table holds exactly
+// taking its measured label; 0 the measured table (LB_SELECTOR=table, or no
+// trained network for the dtype).
+int selector_mode(int dtype)
 {
+    const bool net = dtype >= 0 && dtype < 3 && kMlpPresent[dtype];
     const char *e = std::getenv("LB_SELECTOR");
-    if (e && std::strcmp(e, "table") == 0) return false;
-    return dtype >= 0 && dtype < 3 && kMlpPresent[dtype];
+    if (!net || (e && std::strcmp(e, "table") == 0)) return 0;
+    return 1;
 }
 
 std::atomic<int> g_cu_cache[64];
@@ -146,44 +154,125 @@ int lb::device_cu_count(int *out)
 
 namespace {
 
-// Nearest measured shape of the table in log2(M, N, K) space (L1 distance).
-// The table's logarithms are taken once.
-struct TablePoint {
-    double lm, ln, lk;
-    int dtype, best, second;
+// The table's grid per dtype: its sorted coordinates (log2 M, log2 N, K) and
+// the entry at each grid point (-1 if not measured).  Built once.
+constexpr int kGridMax = 24;
+struct Grid {
+    int nm = 0, nn = 0, nk = 0;
+    int lm[kGridMax], ln[kGridMax], k[kGridMax];
+    int entry[kGridMax][kGridMax][kGridMax];
 };
 
-const TablePoint *table_points()
+void grid_insert(int *vals, int &n, int v)
 {
-    static const TablePoint *pts = [] {
-        TablePoint *p = new TablePoint[kTableLen > 0 ? kTableLen : 1];
-        for (int i = 0; i < kTableLen; ++i) {
-            const SelEntry &e = kTable[i];
-            p[i] = {(double)e.log2m, (double)e.log2n, std::log2((double)e.k), e.dtype, e.best, e.second};
-        }
-        return p;
-    }();
-    return pts;
+    for (int i = 0; i < n; ++i)
+        if (vals[i] == v) return;
+    if (n == kGridMax) return;
+    int i = n++;
+    while (i > 0 && vals[i - 1] > v) { vals[i] = vals[i - 1]; --i; }
+    vals[i] = v;
 }
 
+int grid_index(const int *vals, int n, int v)
+{
+    for (int i = 0; i < n; ++i)
+        if (vals[i] == v) return i;
+    return -1;
+}
+
+const Grid *grids()
+{
+    static const Grid *g = [] {
+        Grid *gs = new Grid[3];
+        for (int i = 0; i < kTableLen; ++i) {
+            const SelEntry &e = kTable[i];
+            if (e.dtype < 0 || e.dtype > 2) continue;
+            Grid &G = gs[e.dtype];
+            grid_insert(G.lm, G.nm, e.log2m);
+            grid_insert(G.ln, G.nn, e.log2n);
+            grid_insert(G.k, G.nk, e.k);
+        }
+        for (int d = 0; d < 3; ++d)
+            for (int a = 0; a < kGridMax; ++a)
+                for (int b = 0; b < kGridMax; ++b)
+                    for (int c = 0; c < kGridMax; ++c) gs[d].entry[a][b][c] = -1;
+        for (int i = 0; i < kTableLen; ++i) {
+            const SelEntry &e = kTable[i];
+            if (e.dtype < 0 || e.dtype > 2) continue;
+            Grid &G = gs[e.dtype];
+            const int a = grid_index(G.lm, G.nm, e.log2m), b = grid_index(G.ln, G.nn, e.log2n),
+                      c = grid_index(G.k, G.nk, e.k);
+            if (a >= 0 && b >= 0 && c >= 0) G.entry[a][b][c] = i;
+        }
+        return gs;
+    }();
+    return g;
+}
+
+// Indices of the grid values bracketing x (one index at or beyond an end, or
+// on a grid value; else the two neighbours).  Returns how many (0 if empty).
+int bracket(const int *vals, int n, double x, bool log_vals, int out[2])
+{
+    if (n == 0) return 0;
+    auto v = [&](int i) { return log_vals ? (double)vals[i] : std::log2((double)vals[i]); };
+    if (x <= v(0)) { out[0] = 0; return 1; }
+    if (x >= v(n - 1)) { out[0] = n - 1; return 1; }
+    int i = 0;
+    while (v(i + 1) <= x) ++i;
+    out[0] = i;
+    if (v(i) == x) return 1;
+    out[1] = i + 1;
+    return 2;
+}
+
+// Each variant's worst time over the measured shapes bracketing (M, N, K),
+// relative to each shape's fastest, in thousandths.  Returns the number of
+// measured shapes found (0: no data for the dtype).
+int bracket_costs(int dtype, int64_t M, int64_t N, int64_t K, int cost[LB_NUM_VARIANTS])
+{
+    for (int v = 0; v < LB_NUM_VARIANTS; ++v) cost[v] = 0;
+    if (dtype < 0 || dtype > 2) return 0;
+    const Grid &G = grids()[dtype];
+    int im[2], in[2], ik[2];
+    const int cm = bracket(G.lm, G.nm, std::log2((double)M), true, im);
+    const int cn = bracket(G.ln, G.nn, std::log2((double)N), true, in);
+    const int ck = bracket(G.k, G.nk, std::log2((double)K), false, ik);
+    int found = 0;
+    for (int a = 0; a < cm; ++a)
+        for (int b = 0; b < cn; ++b)
+            for (int c = 0; c < ck; ++c) {
+                const int e = G.entry[im[a]][in[b]][ik[c]];
+                if (e < 0) continue;
+                ++found;
+                for (int v = 0; v < LB_NUM_VARIANTS; ++v)
+                    if (kTable[e].regret[v] > cost[v]) cost[v] = kTable[e].regret[v];
+            }
+    return found;
+}
+
+// The table's choice: lowest worst-case cost, where costs within 2% of the
+// lowest tie (as the labels do: a tie goes to the default, else to the lower
+// index), and the next lowest.
 void table_choice(int dtype, int64_t M, int64_t N, int64_t K, int *best, int *second)
 {
-    const TablePoint *pts = table_points();
-    const double lm = std::log2((double)M), ln = std::log2((double)N), lk = std::log2((double)K);
-    int bi = -1;
-    double bd = 1e300;
-    for (int i = 0; i < kTableLen; ++i) {
-        if (pts[i].dtype != dtype) continue;
-        const double d = std::fabs(lm - pts[i].lm) + std::fabs(ln - pts[i].ln) + std::fabs(lk - pts[i].lk);
-        if (d < bd) { bd = d; bi = i; }
-    }
-    if (bi < 0) {
+    int cost[LB_NUM_VARIANTS];
+    if (bracket_costs(dtype, M, N, K, cost) == 0) {
         *best = LB_DEFAULT_VARIANT;
         *second = LB_DEFAULT_VARIANT + 1;
         return;
     }
-    *best = pts[bi].best;
-    *second = pts[bi].second;
+    int lo = cost[0];
+    for (int v = 1; v < LB_NUM_VARIANTS; ++v)
+        if (cost[v] < lo) lo = cost[v];
+    int b0 = -1;
+    if (50 * cost[LB_DEFAULT_VARIANT] <= 51 * lo) b0 = LB_DEFAULT_VARIANT;
+    for (int v = 0; v < LB_NUM_VARIANTS && b0 < 0; ++v)
+        if (50 * cost[v] <= 51 * lo) b0 = v;
+    int b1 = -1;
+    for (int v = 0; v < LB_NUM_VARIANTS; ++v)
+        if (v != b0 && (b1 < 0 || cost[v] < cost[b1])) b1 = v;
+    *best = b0;
+    *second = b1;
 }
 
 // The measured label when (M, N, K) is itself a shape of the table (a shape
@@ -241,7 +330,7 @@ int select_from_table(int dtype, int64_t M, int64_t N, int64_t K, int cu_count, 
         int st = lb::device_cu_count(&cu_count);
         if (st != LB_OK) return st;
     }
-    const int mode = use_mlp(dtype) ? 1 : 0;
+    const int mode = selector_mode(dtype);
     const uint64_t h = (uint64_t)M * 0x9E3779B97F4A7C15ull ^ (uint64_t)N * 0xC2B2AE3D27D4EB4Full ^
                        (uint64_t)K * 0x165667B19E3779F9ull ^ (uint64_t)(dtype * 3 + mode) ^ (uint64_t)cu_count;
     CacheSlot &c = t_cache[(h >> 32) & 15u];

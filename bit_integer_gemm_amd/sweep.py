@@ -210,27 +210,37 @@ def labels(recs, eps=EPS, default=DEFAULT):
     for key, ts in shapes.items():
         if any(t is None for t in ts):
             continue
-        order = sorted(range(9), key=lambda v: (ts[v], v))
-        # Variants within eps of the fastest are ties: the default wins a tie,
-        # then the lowest index (fewest stages, then smallest tile), so labels
-        # do not follow timing noise between near-equal variants.
-        tied = [v for v in range(9) if ts[v] <= (1 + eps) * ts[order[0]]]
+        # On the times over the fastest in thousandths, as the library stores
+        # them: variants within eps of the fastest are ties, the default wins a
+        # tie, then the lowest index (fewest stages, then smallest tile), so
+        # labels do not follow timing noise between near-equal variants.
+        r = regret_permille(ts)
+        order = sorted(range(9), key=lambda v: (r[v], v))
+        tied = [v for v in range(9) if r[v] <= (1 + eps) * r[order[0]]]
         best = default if default in tied else min(tied)
         second = next(v for v in order if v != best)
         out[key] = (best, second, ts)
     return out
 
 
+def regret_permille(ts):
+    """Each variant's time over the fastest, in thousandths (capped at 65535)."""
+    t0 = min(ts)
+    return [min(65535, int(round(1000.0 * t / t0))) for t in ts]
+
+
 def write_table(lab, path=TABLE):
     lines = ["// Generated by bit_integer_gemm_amd/sweep.py -- do not edit by hand.",
              "// Labels from variant timings measured on MI355X (median of HIP-event timings).",
-             "// {dtype, log2(M), log2(N), K, best variant, second variant}",
+             "// {dtype, log2(M), log2(N), K, best variant, second variant,",
+             "//  each variant's time over the fastest in thousandths}",
              "static const SelEntry kTable[] = {"]
     items = sorted(lab.items())
-    for (d, M, N, K), (b, s, _) in items:
-        lines.append(f"    {{{DTYPES[d]}, {int(math.log2(M))}, {int(math.log2(N))}, {K}, {b}, {s}}},")
+    for (d, M, N, K), (b, s, ts) in items:
+        r = ", ".join(str(x) for x in regret_permille(ts))
+        lines.append(f"    {{{DTYPES[d]}, {int(math.log2(M))}, {int(math.log2(N))}, {K}, {b}, {s}, {{{r}}}}},")
     if not items:
-        lines.append("    {-1, 0, 0, 1, 7, 8},")
+        lines.append("    {-1, 0, 0, 1, 7, 8, {1000, 1000, 1000, 1000, 1000, 1000, 1000, 1000, 1000}},")
     lines.append("};")
     lines.append(f"static const int kTableLen = {len(items)};")
     with open(path, "w") as f:
@@ -441,7 +451,7 @@ def run_heldout(dtype, out_path, shapes=None, log=print, passes=2, auto=True):
 def library_choices(rows, cu=256):
     """What the built library selects for each row's shape, in both modes
     (host-only queries, no GPU needed): the network (the default) and the
-    table of measured labels (LB_SELECTOR=table)."""
+    measured table (LB_SELECTOR=table)."""
     import bit_integer_gemm_amd as lb
     lb.load()
     old = os.environ.pop("LB_SELECTOR", None)

@@ -24,8 +24,16 @@ TABLE = os.path.join(os.path.dirname(lb.__file__), "csrc", "selector_table.inc")
 def table_entries():
     text = open(TABLE).read()
     n = int(re.search(r"kTableLen = (\d+);", text).group(1))
-    rows = re.findall(r"\{(-?\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\}", text)
-    return [tuple(int(x) for x in r) for r in rows][:n]
+    rows = re.findall(r"\{(-?\d+), (\d+), (\d+), (\d+), (\d+), (\d+), \{([\d, ]+)\}\}", text)
+    return [tuple(int(x) for x in r[:6]) for r in rows][:n]
+
+
+def table_regrets():
+    """{(dtype, log2 M, log2 N, K): nine times over the fastest, in thousandths}"""
+    text = open(TABLE).read()
+    n = int(re.search(r"kTableLen = (\d+);", text).group(1))
+    rows = re.findall(r"\{(-?\d+), (\d+), (\d+), (\d+), (\d+), (\d+), \{([\d, ]+)\}\}", text)[:n]
+    return {tuple(int(x) for x in r[:4]): [int(x) for x in r[6].split(",")] for r in rows}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -71,19 +79,61 @@ def test_measured_shapes_keep_their_labels_in_network_mode():
     assert lb.lb_select_variant(d, 2 ** lm, 2 ** ln, k, 304) == selector_mlp.choose(nets[d], 2 ** lm, 2 ** ln, k, 304)
 
 
-def test_off_grid_shapes_take_nearest_label(table_mode):
-    ents = table_entries()
+def bracket(vals, x):
+    """Grid values bracketing x in log2 (one at or beyond an end or on a value)."""
+    lv = [math.log2(v) for v in vals]
+    lx = math.log2(x)
+    if lx <= lv[0]:
+        return [vals[0]]
+    if lx >= lv[-1]:
+        return [vals[-1]]
+    i = max(j for j in range(len(vals)) if lv[j] <= lx)
+    return [vals[i]] if lv[i] == lx else [vals[i], vals[i + 1]]
+
+
+def test_off_grid_shapes_take_the_bracketing_minimax(table_mode):
+    """Table mode: the variant with the lowest worst relative time over the
+    measured shapes bracketing (M, N, K) (ties within 2% to the default, else
+    the lowest index), recomputed here from the table's stored times."""
+    reg = table_regrets()
     g = np.random.Generator(np.random.PCG64(5))
     for _ in range(300):
         d = int(g.integers(0, 3))
         M, N = int(g.integers(1, 40000)), int(g.integers(1, 40000))
         K = int(g.integers(1, 70000))
-        cand = [e for e in ents if e[0] == d]
-        dist = [abs(math.log2(M) - e[1]) + abs(math.log2(N) - e[2]) + abs(math.log2(K) - math.log2(e[3]))
-                for e in cand]
-        best = min(dist)
-        ok = {(e[4], e[5]) for e, dd in zip(cand, dist) if dd <= best + 1e-9}
-        assert lb.lb_select_variant(d, M, N, K, 256) in ok, (d, M, N, K)
+        Ms = sorted({2 ** k[1] for k in reg if k[0] == d})
+        Ns = sorted({2 ** k[2] for k in reg if k[0] == d})
+        Ks = sorted({k[3] for k in reg if k[0] == d})
+        corners = [(d, int(math.log2(m)), int(math.log2(n)), k)
+                   for m in bracket(Ms, M) for n in bracket(Ns, N) for k in bracket(Ks, K)]
+        cost = [max(reg[c][v] for c in corners) for v in range(9)]
+        lo = min(cost)
+        tied = [v for v in range(9) if 50 * cost[v] <= 51 * lo]
+        best = 7 if 7 in tied else min(tied)
+        assert lb.lb_select_variant(d, M, N, K, 256)[0] == best, (d, M, N, K)
+
+
+def test_bracketing_uses_the_neighbours_worst_case(table_mode):
+    """A shape between two grid K values takes a variant that is good at both,
+    not the label of the nearer one when that label is poor at the other."""
+    reg = table_regrets()
+    hit = 0
+    for (d, lm, ln, k), r in reg.items():
+        ks = sorted({kk[3] for kk in reg if kk[0] == d})
+        i = ks.index(k)
+        if i + 1 >= len(ks):
+            continue
+        k2 = ks[i + 1]
+        r2 = reg[(d, lm, ln, k2)]
+        lab = min(range(9), key=lambda v: (r[v], v))
+        if r2[lab] < 1300:
+            continue
+        # just above k, nearer to k than to k2 in log2
+        K = int(2 ** (math.log2(k) + 0.25 * (math.log2(k2) - math.log2(k))))
+        v = lb.lb_select_variant(d, 2 ** lm, 2 ** ln, K, 256)[0]
+        assert max(r[v], r2[v]) <= max(r[lab], r2[lab]), ((d, lm, ln, K), v, lab)
+        hit += 1
+    assert hit > 0
 
 
 def test_selector_argument_errors():
@@ -200,14 +250,18 @@ def test_repeated_queries_and_mode_switches_agree():
     for _ in range(3):
         for s in shapes:
             assert lb.lb_select_variant(*s, 256) == net[s]
-    # the table answers still follow the nearest-shape rule checked above
-    ents = table_entries()
+    # the table answers still follow the bracketing rule checked above
+    reg = table_regrets()
     for (d, M, N, K), got in table.items():
-        cand = [e for e in ents if e[0] == d]
-        dist = lambda e: (abs(math.log2(M) - e[1]) + abs(math.log2(N) - e[2])  # noqa: E731
-                          + abs(math.log2(K) - math.log2(e[3])))
-        best = min(dist(e) for e in cand)
-        assert got in {(e[4], e[5]) for e in cand if abs(dist(e) - best) < 1e-12}
+        Ms = sorted({2 ** k[1] for k in reg if k[0] == d})
+        Ns = sorted({2 ** k[2] for k in reg if k[0] == d})
+        Ks = sorted({k[3] for k in reg if k[0] == d})
+        corners = [(d, int(math.log2(m)), int(math.log2(n)), k)
+                   for m in bracket(Ms, M) for n in bracket(Ns, N) for k in bracket(Ks, K)]
+        cost = [max(reg[c][v] for c in corners) for v in range(9)]
+        lo = min(cost)
+        tied = [v for v in range(9) if 50 * cost[v] <= 51 * lo]
+        assert got[0] == (7 if 7 in tied else min(tied))
     # the two modes really differ somewhere, so the test can see a stale answer
     assert any(table[s] != net[s] for s in shapes)
 
