@@ -42,6 +42,9 @@ AB_BUILDS = {
     "no_swizzle": ["-DLB_AB_LDS_SWIZZLE=0"],
     "rows_spread": ["-DLB_AB_COPY_ROWS_SPREAD=1"],
     "plain_tile_map": ["-DLB_AB_TILE_MAP_PLAIN=1"],
+    "copy_burst": ["-DLB_AB_COPY_BURST=1"],
+    "w4_int8_only": ["-DLB_AB_W4_INT8_ONLY=1"],
+    "w4_bands": ["-DLB_AB_W4_BANDS=1"],
 }
 AB_DIR = os.path.join(PKG, "ab")
 

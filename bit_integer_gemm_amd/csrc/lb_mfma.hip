@@ -96,12 +96,31 @@ struct MfmaCfg {
 //                           16 different rows instead of 4 lanes per row
 //   LB_AB_TILE_MAP_PLAIN=1  workgroups take tiles in row-major order (no XCD
 //                           runs, no bands)
+//   LB_AB_COPY_BURST=1      four-wave int8 tile: a refill's 16 copies per
+//                           wave all go out in the odd block's second half,
+//                           one per two MFMAs (instead of one per four over
+//                           that half and the next block's first half)
+//   LB_AB_W4_INT8_ONLY=1    int4 and 1-bit large 2-stage variant on the 8-wave
+//                           tile of the general kernel instead of the
+//                           four-wave tile
+//   LB_AB_W4_BANDS=1        four-wave tile: XCD runs and bands of tile rows for
+//                           every grid width (not row-major order when the
+//                           width is a multiple of 8 tiles)
 // Each keeps the results exact; only the speed changes.
 #ifndef LB_AB_LDS_SWIZZLE
 #define LB_AB_LDS_SWIZZLE 1
 #endif
 #ifndef LB_AB_COPY_ROWS_SPREAD
 #define LB_AB_COPY_ROWS_SPREAD 0
+#endif
+#ifndef LB_AB_COPY_BURST
+#define LB_AB_COPY_BURST 0
+#endif
+#ifndef LB_AB_W4_INT8_ONLY
+#define LB_AB_W4_INT8_ONLY 0
+#endif
+#ifndef LB_AB_W4_BANDS
+#define LB_AB_W4_BANDS 0
 #endif
 
 // Layout of a 16-row x 64-byte block: row r's chunk c sits at 16-byte slot
@@ -613,11 +632,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave >> 1, wn = wave & 1u;
-    // Bands of 4 tile rows: against 8, int8 8192 x 8192 x 4096 241.6 against
-    // 283.9 us and 16384 x 4096 x 4096 233.6 against 236.7 us, 4096^3 equal
-    // (bands of 2: 239.6, 267.2, 59.1 us).
+    // A grid whose width is a multiple of 8 tiles takes tiles in row-major
+    // order: round robin over the XCDs then gives each XCD every eighth column
+    // of the same rows, and measured against the XCD runs with bands of 4 rows
+    // this was faster (same-box interleaved timings, int8: 4096 x 16384 x 4096
+    // 235.2 against 263.6 us, 8192^2 x 4096 251.7 against 261.6 us, 8192^2 x
+    // 8192 429.9 against 443.8 us, 4096^3 64.7 against 65.2 us; int4 4096^3
+    // 55.9 against 56.7 us; 16384 x 4096 and 12288^2 within 1%).  Other widths
+    // keep the XCD runs and bands (the linear layer's 43 tile columns: 359.2
+    // against 368.8 us for row-major), bands of 4 tile rows: against 8, int8
+    // 8192 x 8192 x 4096 241.6 against 283.9 us and 16384 x 4096 x 4096 233.6
+    // against 236.7 us, 4096^3 equal (bands of 2: 239.6, 267.2, 59.1 us).
     uint32_t tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4u, tm, tn);
+    if (tiles_n % 8u == 0u && !LB_AB_W4_BANDS) {
+        tm = blockIdx.x / tiles_n;
+        tn = blockIdx.x % tiles_n;
+    } else {
+        tile_of_block(blockIdx.x, tiles_m, tiles_n, 4u, tm, tn);
+    }
     const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
 
     // Split K as in the other kernels: row blockIdx.y of the grid sums K bytes
@@ -744,7 +776,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 mfma_tied(acc[i][j], fb[j], fa[i]);
-                if (CP && j % 4 == 0) copy_r((second ? 0 : 8) + (i - i0) * 2 + j / 4);
+                if (LB_AB_COPY_BURST) {
+                    if (CP && second && j % 2 == 0) copy_r((i - i0) * 4 + j / 2);
+                } else if (CP && j % 4 == 0) {
+                    copy_r((second ? 0 : 8) + (i - i0) * 2 + j / 4);
+                }
                 if (second && j % 2 == 1) {
                     const int q = (i - i0) * 4 + j / 2;  // 0..15
                     if (q < FN) nb[q] = *(const i32x4 *)(f + 32768 + (wn * FN + q) * 2048);
@@ -757,7 +793,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     i32x4 *nb) {
         constexpr int PAR = decltype(par_c)::value;
         constexpr bool FIRST = decltype(first_c)::value;
-        half(std::integral_constant<bool, PAR == 0 && !FIRST>{}, ca, cb, 0, false, nullptr, na, nb);
+        half(std::integral_constant<bool, PAR == 0 && !FIRST && !LB_AB_COPY_BURST>{}, ca, cb, 0, false, nullptr, na, nb);
         if constexpr (PAR == 1) {
             wait_vm_barrier<0>();
             const int ss = t / 2;
@@ -1196,7 +1232,8 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
         // int8 and int4 GEMMs and the linear layer: the four-wave large tile
         // (same 256x256 tile, two stages of 128 K-bytes).  1-bit: 8 waves of
         // 64x128; the convolution: 16 waves of 64x64.
-        if constexpr ((KIND == KIND_S8 || KIND == KIND_S4 || KIND == KIND_LINEAR || KIND == KIND_B1F4) && !CONV)
+        if constexpr ((KIND == KIND_S8 || KIND == KIND_LINEAR ||
+                       ((KIND == KIND_S4 || KIND == KIND_B1F4) && !LB_AB_W4_INT8_ONLY)) && !CONV)
             return launch_w4<KIND>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
         else
             return launch_one<std::conditional_t<b1 || (KIND == KIND_S4 && !CONV), L2W8, L2W16>, KIND, CONV>(
