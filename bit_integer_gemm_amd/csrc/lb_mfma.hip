@@ -105,7 +105,7 @@ struct MfmaCfg {
 //                           four-wave tile
 //   LB_AB_W4_BANDS=1        four-wave tile: XCD runs and bands of tile rows for
 //                           every grid width (not row-major order when the
-//                           width is a multiple of 8 tiles)
+//                           width is a multiple of 64 tiles)
 // Each keeps the results exact; only the speed changes.
 #ifndef LB_AB_LDS_SWIZZLE
 #define LB_AB_LDS_SWIZZLE 1
@@ -632,19 +632,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave >> 1, wn = wave & 1u;
-    // A grid whose width is a multiple of 8 tiles takes tiles in row-major
-    // order: round robin over the XCDs then gives each XCD every eighth column
-    // of the same rows, and measured against the XCD runs with bands of 4 rows
-    // this was faster (same-box interleaved timings, int8: 4096 x 16384 x 4096
-    // 235.2 against 263.6 us, 8192^2 x 4096 251.7 against 261.6 us, 8192^2 x
-    // 8192 429.9 against 443.8 us, 4096^3 64.7 against 65.2 us; int4 4096^3
-    // 55.9 against 56.7 us; 16384 x 4096 and 12288^2 within 1%).  Other widths
-    // keep the XCD runs and bands (the linear layer's 43 tile columns: 359.2
-    // against 368.8 us for row-major), bands of 4 tile rows: against 8, int8
-    // 8192 x 8192 x 4096 241.6 against 283.9 us and 16384 x 4096 x 4096 233.6
-    // against 236.7 us, 4096^3 equal (bands of 2: 239.6, 267.2, 59.1 us).
+    // A grid 64 tiles wide (or a multiple) takes tiles in row-major order:
+    // round robin over the XCDs then gives each XCD every eighth column of
+    // the same rows.  Same-box interleaved timings against the XCD runs with
+    // bands of 4 rows, int8: 4096 x 16384 x 4096 243.1 against 270.0 us,
+    // 16384^2 x 4096 961 against 1058 us; 32 tiles wide it was mixed (8192^2 x
+    // 4096 251.4 against 260.8 us, but 2048 x 8192 x 4096 60.8 against 58.3 us
+    // and int4 16384 x 8192 x 8192 715 against 701 us); 16 wide equal within
+    // 1% (4096^3, where it read 50% more bytes past L2), 48 wide 0.6% slower,
+    // 43 wide (the linear layer) 2.7% slower.  Other grids keep the XCD runs
+    // and bands of 4 tile rows: against 8, int8 8192 x 8192 x 4096 241.6
+    // against 283.9 us and 16384 x 4096 x 4096 233.6 against 236.7 us, 4096^3
+    // equal (bands of 2: 239.6, 267.2, 59.1 us).
     uint32_t tm, tn;
-    if (tiles_n % 8u == 0u && !LB_AB_W4_BANDS) {
+    if (tiles_n % 64u == 0u && !LB_AB_W4_BANDS) {
         tm = blockIdx.x / tiles_n;
         tn = blockIdx.x % tiles_n;
     } else {

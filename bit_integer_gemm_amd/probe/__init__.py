@@ -14,6 +14,14 @@ worth converting to.
 XCD's do, and when one in eight of every XCD's do (256 KiB each, the int32
 tile of a 256 x 256 GEMM tile), to tell a per-XCD limit from a chip-wide one.
 
+4. Cycles per MFMA slot (s_memtime, per wave) of one wave per SIMD issuing V
+vector instructions (a masking AND, a 64-bit shift) or s_nop 1 after each of
+its own MFMAs: how many unpack instructions fit between a wave's MFMAs.
+
+5. Cycles per MFMA of waves that also issue direct global->LDS copies between
+their MFMAs (one wave per SIMD; copies in all four waves or in one): the cost
+of a copy to its wave, and where the CU's copy path saturates.
+
   python -m bit_integer_gemm_amd.probe          # prints one JSON object
 """
 from __future__ import annotations
@@ -120,7 +128,76 @@ def measure_stores(chunk_bytes: int = 256 << 10, reps: int = 5) -> dict:
     return out
 
 
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def measure_slots(iters: int = 1000) -> dict:
+    """Cycles per MFMA slot of one wave per SIMD with V other instructions
+    after each MFMA (median over the waves)."""
+    import torch
+    lib = ctypes.CDLL(LIB)
+    lib.slot_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.slot_run.restype = ctypes.c_int
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    cyc = torch.zeros(cu * 4, dtype=torch.int32, device="cuda")
+    buf = torch.empty(cu * 256, dtype=torch.float32, device="cuda")
+    names = {0: "v_and_b32 (SGPR mask)", 1: "v_lshlrev_b64", 2: "s_nop 1"}
+    out = {}
+    base = None
+    for op, v in ((0, 0), (0, 1), (0, 2), (0, 3), (0, 4), (0, 8), (1, 1), (1, 2), (2, 1), (2, 2)):
+        for _ in range(2):
+            if lib.slot_run(op, v, cu, iters, ctypes.c_void_p(cyc.data_ptr()), ctypes.c_void_p(buf.data_ptr())) != 0:
+                raise RuntimeError("slot probe failed")
+        c = _median([x & 0xFFFFFFFF for x in cyc.cpu().tolist()]) / (16 * iters)
+        if v == 0:
+            base = c
+        key = "none" if v == 0 else f"{names[op]} x{v}"
+        out[key] = {"cycles_per_mfma_slot": round(c, 2), "extra_cycles": round(c - base, 2)}
+        print(f"[probe] slots: {key}: {c:.2f} cycles per MFMA slot", flush=True)
+    return out
+
+
+def measure_copies(iters: int = 500) -> dict:
+    """Cycles per MFMA of one wave per SIMD issuing copies between its MFMAs:
+    (MFMAs per copy group, copies per group) x (all waves copy, wave 0 only)."""
+    import torch
+    lib = ctypes.CDLL(LIB)
+    lib.copy_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.copy_run.restype = ctypes.c_int
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    n = 2 << 20
+    src = torch.randint(-128, 128, (n + (128 << 10),), dtype=torch.int8, device="cuda")
+    cyc = torch.zeros(cu * 4, dtype=torch.int32, device="cuda")
+    buf = torch.empty(cu * 256, dtype=torch.float32, device="cuda")
+    out = {}
+    for _ in range(2):   # mode 0: no wave copies (the MFMA-only baseline)
+        if lib.copy_run(8, 1, ctypes.c_void_p(src.data_ptr()), n - 1, 0, cu, iters,
+                        ctypes.c_void_p(cyc.data_ptr()), ctypes.c_void_p(buf.data_ptr())) != 0:
+            raise RuntimeError("copy probe failed")
+    base = _median([x & 0xFFFFFFFF for x in cyc.cpu().tolist()]) / (32 * iters)
+    out["no copies"] = {"cycles_per_mfma_wave0": round(base, 2), "copies_per_mfma": 0.0}
+    print(f"[probe] copies: none: {base:.2f} cycles per MFMA", flush=True)
+    for cpm, burst in ((16, 1), (8, 1), (4, 1), (2, 1), (8, 2), (16, 4), (32, 8)):
+        for mode, who in ((1, "all waves"), (2, "wave 0 only")):
+            for _ in range(2):
+                if lib.copy_run(cpm, burst, ctypes.c_void_p(src.data_ptr()), n - 1, mode, cu, iters,
+                                ctypes.c_void_p(cyc.data_ptr()), ctypes.c_void_p(buf.data_ptr())) != 0:
+                    raise RuntimeError("copy probe failed")
+            w = [x & 0xFFFFFFFF for x in cyc.cpu().tolist()]
+            c0 = _median(w[0::4]) / (32 * iters)
+            key = f"{burst} copies per {cpm} MFMAs, {who}"
+            per_copy = (c0 - base) * cpm / burst
+            out[key] = {"cycles_per_mfma_wave0": round(c0, 2), "copies_per_mfma": burst / cpm,
+                        "cycles_per_copy": round(per_copy, 1)}
+            print(f"[probe] copies: {key}: wave 0 {c0:.2f} cycles per MFMA, {per_copy:.1f} per copy", flush=True)
+    return out
+
+
 def main():
     if not os.path.exists(LIB):
         sys.exit(f"{LIB} not built: run __graft_entry__.build() or bit_integer_gemm_amd.probe.build()")
-    print(json.dumps({"mfma": measure(), "mix": measure_mix(), "stores": measure_stores()}))
+    print(json.dumps({"mfma": measure(), "mix": measure_mix(), "stores": measure_stores(),
+                      "slots": measure_slots(), "copies": measure_copies()}))

@@ -15,6 +15,15 @@
 // staggering tiles in time can hide it.
 //
 // 3. (below) MFMA throughput with independent vector instructions between.
+//
+// 4. (below) Cycles per MFMA slot of one wave that issues V other instructions
+// after each MFMA: the cost of a vector instruction placed between a wave's own
+// MFMAs, which decides how the int4 and 1-bit plane unpack is spread.
+//
+// 5. (below) Cycles per MFMA of a wave that also issues direct global->LDS
+// copies (16 bytes per lane) between its MFMAs, B copies after every CPM-th
+// MFMA, in all four waves of a workgroup or in wave 0 only: the cost of a copy
+// to its wave, and the CU's copy bandwidth once copies collide.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -142,7 +151,160 @@ __global__ __launch_bounds__(256) void store_kernel(i32x4 *out, int chunk_vec, i
     for (int i = threadIdx.x; i < chunk_vec; i += 256) p[i] = v;
 }
 
+// 4. OP 0: v_and_b32 with an SGPR mask (the unpack's masking), 1: 64-bit
+// shift (v_lshlrev_b64), 2: s_nop 1; V instructions after each MFMA, on
+// registers no MFMA reads.  Per-wave cycles (s_memtime) into cyc[wave].
+template <int OP, int V>
+__global__ __launch_bounds__(256) void slot_kernel(int iters, uint32_t msk, uint32_t *cyc, float *out)
+{
+    const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+    const i32x4 a = {(int)mix(gid), (int)mix(gid + 7u), (int)mix(gid * 3u), (int)mix(gid * 5u + 1u)};
+    const i32x4 b = {(int)mix(a[0]), (int)mix(a[1]), (int)mix(a[2]), (int)mix(a[3])};
+    i32x4 acc[16];
+    for (int q = 0; q < 16; ++q) acc[q] = i32x4{0, 0, 0, 0};
+    uint32_t x[8];
+    for (int q = 0; q < 8; ++q) x[q] = gid * (2u * (uint32_t)q + 3u);
+    uint64_t y0 = gid, y1 = gid * 3ull;
+    const uint32_t sm = __builtin_amdgcn_readfirstlane(msk);
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc[q]) : "v"(a), "v"(b));
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if constexpr (OP == 0) asm volatile("v_and_b32 %0, %1, %0" : "+v"(x[v]) : "s"(sm));
+                else if constexpr (OP == 1) {
+                    if (v % 2 == 0) asm volatile("v_lshlrev_b64 %0, 4, %0" : "+v"(y0));
+                    else asm volatile("v_lshlrev_b64 %0, 4, %0" : "+v"(y1));
+                } else asm volatile("s_nop 1");
+            }
+        }
+    }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    float total = (float)(y0 ^ y1);
+    for (int q = 0; q < 8; ++q) total += (float)x[q];
+    for (int q = 0; q < 16; ++q) total += (float)(acc[q][0] + acc[q][1] + acc[q][2] + acc[q][3]);
+    out[gid] = total;
+    if ((threadIdx.x & 63u) == 0) cyc[gid / 64u] = (uint32_t)(t1 - t0);
+}
+
+__device__ inline i32x4 probe_rsrc(const void *base, uint32_t n)
+{
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu));
+    r.z = __builtin_amdgcn_readfirstlane((int)n);
+    r.w = 0x00020000;
+    return r;
+}
+
+// 5. Copies read a 2^k-byte source (plus 128 KiB of slack, which the offsets
+// stay inside) as the GEMM's copies do: 8 lanes per 128-byte line, 8 rows of
+// 4 KiB pitch per copy; each wave writes its own 16 KiB of the 64 KiB LDS.
+// Per iteration 32 MFMAs, and BURST copies after every CPM-th; at most 40
+// copies of a wave stay outstanding.  mode 1: every wave copies; 2: wave 0.
+template <int CPM, int BURST>
+__global__ __launch_bounds__(256) void copy_kernel(const char *src, uint32_t src_mask, int mode, int iters,
+                                                   uint32_t *cyc, float *out)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[65536];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+    const i32x4 a = {(int)mix(gid), (int)mix(gid + 7u), (int)mix(gid * 3u), (int)mix(gid * 5u + 1u)};
+    const i32x4 b = {(int)mix(a[0]), (int)mix(a[1]), (int)mix(a[2]), (int)mix(a[3])};
+    i32x4 acc[16];
+    for (int q = 0; q < 16; ++q) acc[q] = i32x4{0, 0, 0, 0};
+    const i32x4 rs = probe_rsrc(src, src_mask + 1u + 65536u);
+    const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem + wave * 16384u;
+    const bool copies = mode == 1 || (mode == 2 && wave == 0);
+    const uint32_t lo = (lane >> 3) * 4096u + (lane & 7u) * 16u;   // < 32 KiB
+    uint32_t blk = ((blockIdx.x * 4u + wave) * 32768u) & src_mask;
+    uint32_t vo[16];
+    for (int q = 0; q < 16; ++q) vo[q] = lo + (uint32_t)(q % 8) * 128u + (uint32_t)(q / 8) * 32768u;  // < 64 KiB
+    __syncthreads();
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    // (the copying and the non-copying waves run separate loops: a branch
+    // around every copy would cost more than the copy)
+    if (copies) {
+        for (int it = 0; it < iters; ++it) {
+            int n = 0;
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc[q % 16]) : "v"(a), "v"(b));
+                if (q % CPM == CPM - 1) {
+#pragma unroll
+                    for (int c = 0; c < BURST; ++c, ++n) {
+                        const uint32_t soff = __builtin_amdgcn_readfirstlane(blk);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+                        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                                     :
+                                     : "v"(vo[n % 16]), "s"(rs), "s"(lbase + (uint32_t)(n % 16) * 1024u), "s"(soff)
+                                     : "memory", "m0");
+#pragma clang diagnostic pop
+                    }
+                }
+            }
+            blk = (blk + 65536u) & src_mask;
+            asm volatile("s_waitcnt vmcnt(40)" ::: "memory");
+        }
+    } else {
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int q = 0; q < 32; ++q)
+                asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc[q % 16]) : "v"(a), "v"(b));
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    float total = (float)smem[(threadIdx.x * 64u) & 65535u];
+    for (int q = 0; q < 16; ++q) total += (float)(acc[q][0] + acc[q][1] + acc[q][2] + acc[q][3]);
+    out[gid] = total;
+    if (lane == 0) cyc[gid / 64u] = (uint32_t)(t1 - t0);
+}
+
 extern "C" {
+
+// Launch `blocks` workgroups of slot_kernel<op, v>; cyc holds blocks * 4
+// words, out blocks * 256 floats.  0 on success, < 0 on a HIP error or an
+// unknown case.
+int slot_run(int op, int v, int blocks, int iters, uint32_t *cyc, float *out)
+{
+    bool ok = false;
+#define LB_PROBE_SLOT(O, N)                                                                              \
+    if (!ok && op == O && v == N) {                                                                     \
+        ok = true;                                                                                       \
+        hipLaunchKernelGGL((slot_kernel<O, N>), dim3(blocks), dim3(256), 0, 0, iters, 0xF0F0F0F0u, cyc, out); \
+    }
+    LB_PROBE_SLOT(0, 0) LB_PROBE_SLOT(0, 1) LB_PROBE_SLOT(0, 2) LB_PROBE_SLOT(0, 3) LB_PROBE_SLOT(0, 4)
+    LB_PROBE_SLOT(0, 8) LB_PROBE_SLOT(1, 1) LB_PROBE_SLOT(1, 2) LB_PROBE_SLOT(2, 1) LB_PROBE_SLOT(2, 2)
+#undef LB_PROBE_SLOT
+    if (!ok) return -5;
+    return hipDeviceSynchronize() == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Launch `blocks` workgroups of copy_kernel<cpm, burst> over src (mask + 1 +
+// 128 KiB bytes, mask + 1 a power of two); cyc holds blocks * 4 words, out
+// blocks * 256 floats.  0 on success, < 0 on a HIP error or an unknown case.
+int copy_run(int cpm, int burst, const char *src, uint32_t src_mask, int mode, int blocks, int iters,
+             uint32_t *cyc, float *out)
+{
+    bool ok = false;
+#define LB_PROBE_COPY(C, B)                                                                               \
+    if (!ok && cpm == C && burst == B) {                                                                   \
+        ok = true;                                                                                         \
+        hipLaunchKernelGGL((copy_kernel<C, B>), dim3(blocks), dim3(256), 0, 0, src, src_mask, mode, iters, cyc, out); \
+    }
+    LB_PROBE_COPY(2, 1) LB_PROBE_COPY(4, 1) LB_PROBE_COPY(8, 1) LB_PROBE_COPY(16, 1) LB_PROBE_COPY(8, 2)
+    LB_PROBE_COPY(16, 4) LB_PROBE_COPY(32, 8)
+#undef LB_PROBE_COPY
+    if (!ok) return -5;
+    return hipDeviceSynchronize() == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 // Launch `blocks` workgroups of mix_kernel<v_per_mfma> (0..4); out holds
 // blocks * 256 floats.  Milliseconds between HIP events, or < 0 on error.
