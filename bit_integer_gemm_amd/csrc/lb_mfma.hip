@@ -561,12 +561,12 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     }
 }
 
-// ---- large tile on four waves (int8, int4, int8 linear) -----------------
-// The 2-stage large variant of the int8 and int4 GEMMs and the int8 linear
-// layer: a 256x256 tile on four waves (one per SIMD) of 128x128, all 256 int32
-// accumulators of a lane in AGPRs.  Per workgroup, per 64 K-bytes: 64 KiB of
-// LDS fragment reads for 256 MFMAs (512 for int4), against 128 KiB for
-// sixteen waves of 64x64.
+// ---- large tile on four waves (int8, int4, 1-bit, int8 linear) ----------
+// The 2-stage large variant of the int8, int4 and 1-bit (FP4 route) GEMMs and
+// of the int8 linear layer: a 256x256 tile on four waves (one per SIMD) of
+// 128x128, all 256 accumulators of a lane in AGPRs.  Per workgroup, per 64
+// K-bytes: 64 KiB of LDS fragment reads for 256 MFMAs (int4: 512; 1-bit: 1024
+// FP4 MFMAs), against 128 KiB for sixteen waves of 64x64.
 //  * Two LDS super-stages of 128 K-bytes (64 KiB each: 256 A rows, 256 B rows)
 //    form the 2-stage ring.  A 2 KiB block holds 16 rows x 128 bytes as two
 //    1 KiB halves of 8 rows; row r's 16-byte chunk c sits at
@@ -595,12 +595,15 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
 //    is left to load, the copies read an empty buffer range (zeros, no memory
 //    traffic) into the slot just released, which nothing reads again, so the
 //    copy code has no branches (a branch per copy cost several percent).
-//  * int4: the LDS holds packed bytes and each fragment is unpacked in
-//    registers into its even-k and odd-k planes (see s4_even_plane), two
-//    MFMAs per fragment pair.  A row's two A planes are made before its
-//    MFMAs; B's planes are made for the whole block in its first row.  One
-//    wave per SIMD issues its unpack next to its own MFMAs, and every copy
-//    now serves twice the MFMAs of the int8 tile.
+//  * int4 and 1-bit: the LDS holds packed bytes, and each fragment is turned
+//    in registers into the planes the MFMAs take (int4: even-k and odd-k
+//    nibbles, two MFMAs per fragment pair; 1-bit: four FP4 bit planes, four
+//    MFMAs).  With one wave per SIMD nothing else hides that vector work, so
+//    it is written as single-instruction asm statements placed between the
+//    MFMAs (measured: up to two vector instructions per MFMA issue free, each
+//    further one costs about 4 cycles), each plane complete at least two
+//    instructions before the MFMA that reads it.  Every copy serves two
+//    (int4) or four (1-bit) times the MFMAs of the int8 tile.
 //  * The MFMA is inline assembly with the accumulator tied to its AGPR: with
 //    the builtin the compiler picks the untied form and shuffles all 256
 //    accumulators between register files.  Its operands come straight from
@@ -832,7 +835,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         if (t < nk) body(P1{}, F0{}, t, fa1, fb1, fa0, fb0);
     } else if constexpr (KIND == KIND_S4) {
-        // int4.  Per block (256 MFMA slots per wave) 160 vector instructions
+        // int4.  Per block (128 MFMA slots per wave) 160 vector instructions
         // make the even-k and odd-k planes of 16 fragments.  Next to a wave's
         // own MFMAs about two vector instructions per MFMA issue free, and
         // each further one costs about 4 cycles (measured), so they are
@@ -1177,11 +1180,13 @@ using M4 = MfmaCfg<128, 128, 64, 2, 2, 4>;    // 64 KiB
 // Measured per variant, two builds timed in one process: the 3-stage large
 // tile is 1-7% faster with 8 waves for every type, the 4-stage one 2-4% for
 // int4 and mixed for int8, and the 2-stage one mixed for int8 and int4 (the
-// 16 waves win by 4-9% when there are only 16-64 tiles).  The 1-bit kernels
+// 16 waves win by 4-9% when there are only 16-64 tiles).  The 1-bit tiles here
 // use 8 waves throughout: their per-fragment bit work makes the wider wave
 // tile pay at every depth (124 against 137 us at 4096 x 4096 x 8192 bits with
-// the first bit expansion).  The int4 and int8 GEMMs' 2-stage large tile
-// runs on the four-wave kernel (mfma_w4_kernel).
+// the first bit expansion).  The 2-stage large tile of the int8, int4 and
+// 1-bit (FP4 route) GEMMs and of the linear layer runs on the four-wave kernel
+// (mfma_w4_kernel); the 1-bit int8 route and the convolutions keep the
+// kernels above.
 using L2W16 = MfmaCfg<256, 256, 128, 4, 4, 2>; // 128 KiB
 using L2W8 = MfmaCfg<256, 256, 128, 4, 2, 2>;  // 128 KiB
 using L3W8 = MfmaCfg<256, 256, 64, 4, 2, 3>;   // 96 KiB
@@ -1230,9 +1235,11 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     constexpr bool b1 = KIND == KIND_B1 || KIND == KIND_B1F4;
     switch (variant) {
     case 6:
-        // int8 and int4 GEMMs and the linear layer: the four-wave large tile
-        // (same 256x256 tile, two stages of 128 K-bytes).  1-bit: 8 waves of
-        // 64x128; the convolution: 16 waves of 64x64.
+        // int8, int4 and 1-bit (FP4 route) GEMMs and the linear layer: the
+        // four-wave large tile (same 256x256 tile, two stages of 128 K-bytes).
+        // 1-bit on the int8 route: 8 waves of 64x128; the convolutions: 16
+        // waves of 64x64; the int4 GEMM under the A/B switch that keeps the
+        // four-wave kernel to int8: 8 waves of 64x128.
         if constexpr ((KIND == KIND_S8 || KIND == KIND_LINEAR ||
                        ((KIND == KIND_S4 || KIND == KIND_B1F4) && !LB_AB_W4_INT8_ONLY)) && !CONV)
             return launch_w4<KIND>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
