@@ -250,6 +250,9 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     // (medium and large tiles; the small tile keeps its five workgroups per CU
     // and reads the scales from global memory).
     constexpr bool LDS_SCALES = KIND == KIND_LINEAR && C::BM >= 128;
+    // LATE_COPIES (four-wave tiles and int4): the next stage's copies go out
+    // right after the stage wait, ahead of this stage's fragment reads; the
+    // other tiles issue them behind the first fragment reads (see the loop).
     constexpr bool LATE_COPIES = C::NW == 4 || KIND == KIND_S4;
     constexpr int SCALE_BYTES = LDS_SCALES ? (C::BM + C::BN) * 4 : 0;
     __shared__ __attribute__((aligned(1024))) char smem[C::ST * C::STAGE_BYTES + SCALE_BYTES];
@@ -421,8 +424,8 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
             // read, which the barrier above has released), so the LDS latency
             // of the reads runs under the copies' address arithmetic; the MFMAs
             // stay below them.  Measured: 1-2% faster for the large int8 and
-            // 1-bit tiles, 5% slower for the small tile.  The 16-wave int4 tile
-            // copies first: holding its fragments over the copies would spill.
+            // 1-bit tiles, 5% slower for the small tile.  The int4 tiles copy
+            // first: holding their fragments over the copies would spill.
             if (kb == 0) {
                 if constexpr (!LATE_COPIES) {
                     if (kt + C::ST - 1 < nk) issue(kt + C::ST - 1, (int)((kt + C::ST - 1) % C::ST));
