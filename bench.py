@@ -63,6 +63,8 @@ CONV_LAYERS = {
     "s8_conv3x3_n128_14x14x256": ("s8", 128, 14, 14, 256, 256, 3, 3, (1, 1), (1, 1), (6003, 6004)),
     "s4_conv3x3_n128_14x14x256": ("s4", 128, 14, 14, 256, 256, 3, 3, (1, 1), (1, 1), (6005, 6006)),
     "s8_conv1x1_n128_14x14x1024": ("s8", 128, 14, 14, 1024, 256, 1, 1, (1, 1), (0, 0), (6007, 6008)),
+    # 7x7 stride-2 stem with the 3 input channels zero-padded to 16
+    "s8_conv7x7s2_n32_224x224x16": ("s8", 32, 224, 224, 16, 64, 7, 7, (2, 2), (3, 3), (6009, 6010)),
 }
 
 

@@ -35,7 +35,7 @@ K_MAX = {LB_S8: 131071, LB_S4: 131071, LB_B1: 134217600}
 # default, sums in fp32, exact to 2^24; the int8 route, LB_B1_ROUTE=int8, sums 64
 # per pair in int32); longer K runs as K bands (see the header).
 B1_PASS_K = {"fp4": 1 << 24, "int8": 33554304}
-CONV_C_ALIGN = {LB_S8: 64, LB_S4: 128}
+CONV_C_ALIGN = {LB_S8: 16, LB_S4: 32}
 
 # Exported symbols of include/lb_gemm.h (checked by the CPU tests).
 EXPORTS = ("lb_gemm_s8", "lb_gemm_s4", "lb_gemm_b1", "lb_gemm_s8_linear", "lb_conv2d_s8",

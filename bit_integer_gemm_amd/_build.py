@@ -45,6 +45,7 @@ AB_BUILDS = {
     "copy_burst": ["-DLB_AB_COPY_BURST=1"],
     "w4_int8_only": ["-DLB_AB_W4_INT8_ONLY=1"],
     "w4_bands": ["-DLB_AB_W4_BANDS=1"],
+    "reg_staging": ["-DLB_AB_REG_STAGING=1"],
 }
 AB_DIR = os.path.join(PKG, "ab")
 

@@ -66,6 +66,17 @@ __device__ inline void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds_base)
 }
 #pragma clang diagnostic pop
 
+// The same 16 bytes per lane loaded into registers, from a resource made by
+// make_rsrc (for A/B builds that stage operands through registers); offsets
+// >= num_records read zero.
+__device__ inline i32x4 load16(i32x4 rsrc, uint32_t voff)
+{
+    const uint64_t b = (uint64_t)(uint32_t)rsrc.x | ((uint64_t)((uint32_t)rsrc.y & 0xFFFFu) << 32);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)b, (short)0, rsrc.z, rsrc.w);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
 // Wait until at most N of this wave's copies are outstanding and its LDS reads
 // have returned, then barrier: afterwards every wave's copies older than the
 // last N (per wave) are visible in LDS, and no wave still reads the buffer the

@@ -29,7 +29,7 @@ int mfma_variant_info(int kind, int variant, int *bm, int *bn, int *bk_bytes, in
 // Geometry of a convolution run as a GEMM whose A rows are gathered from an
 // NHWC image: output pixel r = (n*Ho + ho)*Wo + wo is row r, the filter taps
 // (kh, kw, channel byte) are the K axis.  Cb is bytes per pixel (C or C/2) and
-// a multiple of 64; x_bytes = N*H*W*Cb < 2^31.
+// a multiple of 16; x_bytes = N*H*W*Cb < 2^31.
 struct ConvGeom {
     int32_t H, W, Cb, Kh, Kw, sh, sw, ph, pw, Ho, Wo;
     uint32_t x_bytes;

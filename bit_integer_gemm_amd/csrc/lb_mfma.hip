@@ -60,9 +60,11 @@
 //    taps (kh, kw) and the channels.  The page's window tensor is never built:
 //    each copy lane reads its 16-byte piece of the window straight from the
 //    NHWC image, the window tensor's addressing without its memory.  Channel
-//    bytes per pixel are a multiple of 64, so one 64-byte K block sits inside
-//    a single tap; pieces that fall in the zero padding (or past M or K) get
-//    an offset with bit 31 set, beyond the buffer range, and load zero.
+//    bytes per pixel are a multiple of 16, so every 16-byte piece sits inside
+//    a single tap (when they are a multiple of 64, a whole 64-byte K block
+//    does, and the tap is the block's); pieces that fall in the zero padding
+//    (or past M or K) get an offset with bit 31 set, beyond the buffer range,
+//    and load zero.
 #include <algorithm>
 #include <type_traits>
 
@@ -106,6 +108,12 @@ struct MfmaCfg {
 //   LB_AB_W4_BANDS=1        four-wave tile: XCD runs and bands of tile rows for
 //                           every grid width (not row-major order when the
 //                           width is a multiple of 64 tiles)
+//   LB_AB_REG_STAGING=1     general kernel: operand stages go global ->
+//                           registers -> LDS (a buffer load into registers
+//                           when the stage is issued, written to LDS at the
+//                           start of the next K step) instead of the direct
+//                           global -> LDS copy; the prologue writes each stage
+//                           at once
 // Each keeps the results exact; only the speed changes.
 #ifndef LB_AB_LDS_SWIZZLE
 #define LB_AB_LDS_SWIZZLE 1
@@ -121,6 +129,9 @@ struct MfmaCfg {
 #endif
 #ifndef LB_AB_W4_BANDS
 #define LB_AB_W4_BANDS 0
+#endif
+#ifndef LB_AB_REG_STAGING
+#define LB_AB_REG_STAGING 0
 #endif
 
 // Layout of a 16-row x 64-byte block: row r's chunk c sits at 16-byte slot
@@ -319,14 +330,21 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
                          (int32_t)blk_chunk_of_lane(lane) * 16;
         }
     }
+    // Advance a (kh, kw, channel byte) position by one 64-byte K block: one tap
+    // when Cb is a multiple of 64, else as many taps as the block crosses
+    // (Cb a multiple of 16: at most four).
     auto next_block = [&](int32_t &kh, int32_t &kw, int32_t &cb) {
         cb += 64;
-        if (cb >= g.Cb) {
-            cb = 0;
+        while (cb >= g.Cb) {
+            cb -= g.Cb;
             if (++kw >= g.Kw) { kw = 0; ++kh; }
         }
     };
 
+    // (A/B build with register staging: the stage issued last, held in
+    // registers until commit() writes it to its LDS slot.)
+    i32x4 stg[LB_AB_REG_STAGING ? C::NDMA : 1];
+    int stg_slot = -1;
     auto issue = [&](int64_t kt, int slot) {
         const int64_t k0 = kt * C::BK;
         i32x4 ra;
@@ -357,13 +375,44 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
 #pragma unroll
                     for (int b = 1; b < C::KB; ++b)
                         if (kb == b) { kh = bkh[b]; kw = bkw[b]; cb = bcb[b]; }
+                    int32_t base = cv_base[i];
+                    if (g.Cb % 64 != 0) {
+                        // Fewer than 64 bytes per tap (or not a multiple): this
+                        // lane's 16-byte chunk lies chunk*16 bytes past the
+                        // block's first byte, up to three taps further on.
+                        const int32_t ch = (int32_t)blk_chunk_of_lane(lane) * 16;
+                        base -= ch;
+                        cb += ch;
+#pragma unroll
+                        for (int w = 0; w < 3; ++w)
+                            if (cb >= g.Cb) {
+                                cb -= g.Cb;
+                                if (++kw >= g.Kw) { kw = 0; ++kh; }
+                            }
+                    }
                     const int32_t hi = cv_hi0[i] + kh, wi = cv_wi0[i] + kw;
                     const bool ok = cv_row[i] && kh < g.Kh && (uint32_t)hi < (uint32_t)g.H &&
                                     (uint32_t)wi < (uint32_t)g.W;
-                    vo = ok ? (uint32_t)(cv_base[i] + (kh * g.W + kw) * g.Cb + cb) : 0x80000000u;
+                    vo = ok ? (uint32_t)(base + (kh * g.W + kw) * g.Cb + cb) : 0x80000000u;
                 }
             }
-            dma16(isA ? ra : rb, vo, dst);
+            if constexpr (LB_AB_REG_STAGING) stg[i] = load16(isA ? ra : rb, vo);
+            else dma16(isA ? ra : rb, vo, dst);
+        }
+        if constexpr (LB_AB_REG_STAGING) stg_slot = slot;
+    };
+    auto commit = [&]() {
+        if constexpr (LB_AB_REG_STAGING) {
+            if (stg_slot >= 0) {
+                char *sb = smem + stg_slot * C::STAGE_BYTES;
+#pragma unroll
+                for (int i = 0; i < C::NDMA; ++i) {
+                    const bool isA = i < C::NDMA_A;
+                    const int j = (int)wave + C::NW * (isA ? i : i - C::NDMA_A);
+                    *(i32x4 *)(sb + (isA ? j : C::ABLK + j) * 1024 + lane * 16) = stg[i];
+                }
+                stg_slot = -1;
+            }
         }
     };
 
@@ -395,12 +444,20 @@ __global__ __launch_bounds__(C::NT) void mfma_gemm_kernel(
     }
 #pragma unroll
     for (int s = 0; s < C::ST - 1; ++s)
-        if (s < nk) issue(s, s);
+        if (s < nk) {
+            issue(s, s);
+            commit();
+        }
 
     for (int64_t kt = 0; kt < nk; ++kt) {
         const int slot = (int)(kt % C::ST);
         const int64_t after = nk - 1 - kt;
-        wait_outstanding<C::NDMA, C::ST>((int)(after < C::ST - 2 ? after : C::ST - 2));
+        if constexpr (LB_AB_REG_STAGING) {
+            commit();
+            barrier_lds();
+        } else {
+            wait_outstanding<C::NDMA, C::ST>((int)(after < C::ST - 2 ? after : C::ST - 2));
+        }
         char *stage = smem + slot * C::STAGE_BYTES;
         if (k_tail && kt == nk - 1) {
             zero_k_tail<C>(stage, lane, wave, kt * C::BK, klen);

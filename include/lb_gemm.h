@@ -152,14 +152,16 @@ int lb_gemm_s8_linear(const int8_t *X, const int8_t *W, const float *sx,
  * allocated.  LB_AUTO picks the variant the GEMM of that shape would get.
  * C must be a multiple of LB_CONV_S8_C_ALIGN (int8) or LB_CONV_S4_C_ALIGN
  * (int4, packed two per byte along C, even c in the low nibble, for X and F
- * alike), else LB_ERR_ALIGN.  LB_ERR_SHAPE for a non-positive size or stride,
+ * alike): 16 bytes per pixel or a multiple, else LB_ERR_ALIGN.  (A layer with
+ * fewer channels, e.g. an RGB input, runs with its channels zero-padded to 16
+ * in X and F; the result is the same.)  LB_ERR_SHAPE for a non-positive size or stride,
  * negative padding or a filter wider than the padded image; LB_ERR_OVERFLOW if
  * Kh*Kw*C exceeds the type's K limit or the padded image or N*Ho*Wo reaches
  * 2^31 (byte offsets are 32-bit).  Pointers, stream and errors otherwise as for
  * the GEMMs.
  */
-#define LB_CONV_S8_C_ALIGN 64
-#define LB_CONV_S4_C_ALIGN 128
+#define LB_CONV_S8_C_ALIGN 16
+#define LB_CONV_S4_C_ALIGN 32
 int lb_conv2d_s8(const int8_t *X, const int8_t *F, int32_t *Y, int64_t N,
                  int64_t H, int64_t W, int64_t C, int64_t Co, int64_t Kh,
                  int64_t Kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw,

@@ -95,7 +95,7 @@ def conv_args(**kw):
     return [d[k] for k in ("N", "H", "W", "C", "Co", "Kh", "Kw", "sh", "sw", "ph", "pw")]
 
 
-@pytest.mark.parametrize("fn,calign", [("lb_conv2d_s8", 64), ("lb_conv2d_s4", 128)])
+@pytest.mark.parametrize("fn,calign", [("lb_conv2d_s8", 16), ("lb_conv2d_s4", 32)])
 def test_conv_argument_checks(lib, fn, calign):
     f = getattr(lib, fn)
     assert f(NULL, FAKE, FAKE, *conv_args(), -1, NULL) == lb.LB_ERR_NULL
@@ -105,13 +105,14 @@ def test_conv_argument_checks(lib, fn, calign):
                 dict(ph=-1), dict(Kh=11), dict(Kw=12, pw=1), dict(H=2**31)):
         assert f(FAKE, FAKE, FAKE, *conv_args(**bad), -1, NULL) == lb.LB_ERR_SHAPE, bad
     assert f(FAKE, FAKE, FAKE, *conv_args(C=calign // 2), -1, NULL) == lb.LB_ERR_ALIGN
-    assert f(FAKE, FAKE, FAKE, *conv_args(C=calign + 16), -1, NULL) == lb.LB_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, *conv_args(C=calign + calign // 2), -1, NULL) == lb.LB_ERR_ALIGN
     assert f(FAKE, FAKE, FAKE, *conv_args(), 9, NULL) == lb.LB_ERR_VARIANT
     assert f(FAKE, FAKE, FAKE, *conv_args(), -2, NULL) == lb.LB_ERR_VARIANT
     # window longer than the exact-int32 K limit
-    assert f(FAKE, FAKE, FAKE, *conv_args(C=calign * 2048, Kh=1, Kw=1, ph=0, pw=0), 0, NULL) == lb.LB_ERR_OVERFLOW
+    assert f(FAKE, FAKE, FAKE, *conv_args(C=calign * 8192, Kh=1, Kw=1, ph=0, pw=0), 0, NULL) == lb.LB_ERR_OVERFLOW
     # padded image of 2^31 bytes or more cannot be addressed with 32-bit offsets
-    big = dict(N=1024, H=256, W=256, C=calign * (1 if calign == 64 else 2), Kh=1, Kw=1, ph=0, pw=0)
+    # 32 bytes per pixel: 1024 x 256 x 256 x 32 = 2^31
+    big = dict(N=1024, H=256, W=256, C=32 if calign == 16 else 64, Kh=1, Kw=1, ph=0, pw=0)
     assert f(FAKE, FAKE, FAKE, *conv_args(**big), 0, NULL) == lb.LB_ERR_OVERFLOW
 
 

@@ -7,7 +7,8 @@ strides, filters (Co, Kh, Kw, C), output NHWC int32.  Every result is an
 integer sum and must match the oracle bit-exactly.
 
 The small cases run every kernel variant and cover ragged output-pixel counts
-and channel counts (not multiples of any tile), non-square filters, unequal
+and channel counts (not multiples of any tile), pixels of 16-48 and 80-112
+bytes (a 64-byte K block then spans several filter taps), non-square filters, unequal
 strides and paddings, padding as wide as the filter (outputs that see only
 padding), a 1x1 filter with stride larger than one and a single-pixel image.
 The layer-sized cases run in the configuration the benchmark times (automatic
@@ -62,7 +63,7 @@ def ref(kind, x, f, C, stride, pad):
     return oracle.conv2d_s4(x, f, C, stride, pad)
 
 
-# (N, H, W, C, Co, Kh, Kw, stride, pad); C is in elements (multiple of 64 / 128)
+# (N, H, W, C, Co, Kh, Kw, stride, pad); C is in elements (64 or more bytes per pixel)
 SMALL = [
     (2, 9, 7, 128, 40, 3, 3, (1, 1), (1, 1)),
     (1, 12, 10, 128, 72, 3, 2, (2, 1), (1, 0)),
@@ -92,6 +93,49 @@ def test_conv_small_all_variants(kind, case):
         np.testing.assert_array_equal(got, want, err_msg=f"{kind} case {case} variant {v}")
 
 
+# Fewer than 64 channel bytes per pixel, or not a multiple of 64: a 64-byte K
+# block spans several filter taps, and each 16-byte piece is gathered from its
+# own tap.  (N, H, W, Cb, Co, Kh, Kw, stride, pad) with Cb in bytes per pixel
+# (int8: C = Cb; int4: C = 2*Cb).
+SMALL_C = [
+    (2, 9, 7, 16, 40, 3, 3, (1, 1), (1, 1)),
+    (1, 12, 10, 32, 72, 3, 2, (2, 1), (1, 0)),
+    (1, 11, 13, 48, 17, 5, 5, (2, 2), (2, 2)),
+    (2, 4, 5, 80, 9, 3, 3, (1, 1), (3, 3)),       # padding wider than the filter reach
+    (1, 6, 3, 16, 130, 1, 7, (1, 1), (0, 3)),     # 1 x 7: a block crosses a filter row
+    (1, 9, 8, 16, 24, 5, 1, (1, 1), (2, 0)),      # 5 x 1: every tap is a new filter row
+    (2, 32, 30, 16, 64, 7, 7, (2, 2), (3, 3)),    # a 7x7 stride-2 stem, RGB padded to 16
+    (1, 5, 5, 112, 33, 2, 2, (1, 1), (0, 0)),
+]
+
+
+@pytest.mark.parametrize("kind", ["s8", "s4"])
+@pytest.mark.parametrize("case", range(len(SMALL_C)))
+def test_conv_few_channels_all_variants(kind, case):
+    N, H, W, Cb, Co, Kh, Kw, st, pd = SMALL_C[case]
+    C = Cb if kind == "s8" else 2 * Cb
+    x, f = make(kind, N, H, W, C, Co, Kh, Kw, 900 + 10 * case)
+    want = ref(kind, x, f, C, st, pd)
+    for v in [lb.LB_AUTO] + list(range(lb.LB_NUM_VARIANTS)):
+        got = run_conv(kind, x, f, st, pd, v)
+        np.testing.assert_array_equal(got, want, err_msg=f"{kind} few-channel case {case} variant {v}")
+
+
+def test_conv_rgb_padded_to_16_channels():
+    """A 3-channel layer run with X and F zero-padded to 16 channels equals the
+    oracle's 3-channel convolution."""
+    N, H, W, Co, Kh, Kw, st, pd = 2, 20, 18, 24, 7, 7, (2, 2), (3, 3)
+    x3 = inputs.s8_nhwc(N, H, W, 3, 950)
+    f3 = inputs.s8_nhwc(Co, Kh, Kw, 3, 951)
+    want = oracle.conv2d_s8(x3, f3, st, pd)
+    x16 = np.zeros((N, H, W, 16), np.int8)
+    x16[..., :3] = x3
+    f16 = np.zeros((Co, Kh, Kw, 16), np.int8)
+    f16[..., :3] = f3
+    for v in (lb.LB_AUTO, 0, 6, 7):
+        np.testing.assert_array_equal(run_conv("s8", x16, f16, st, pd, v), want, err_msg=f"variant {v}")
+
+
 @pytest.mark.parametrize("kind", ["s8", "s4"])
 def test_conv_1x1_matches_gemm_on_gpu(kind):
     """A 1x1, stride-1, unpadded convolution is the GEMM of pixels with filters."""
@@ -108,6 +152,7 @@ def test_conv_1x1_matches_gemm_on_gpu(kind):
 
 # Layer-sized shapes (synthetic; see the design notes for the recipe).
 LAYERS = {
+    "7x7_s2_112x112x16": (4, 112, 112, 16, 64, 7, 7, (2, 2), (3, 3)),   # stem, RGB padded to 16
     "3x3_s1_56x56x64": (8, 56, 56, 64, 64, 3, 3, (1, 1), (1, 1)),
     "3x3_s2_28x28x128": (8, 28, 28, 128, 256, 3, 3, (2, 2), (1, 1)),
     "1x1_14x14x256": (8, 14, 14, 256, 1024, 1, 1, (1, 1), (0, 0)),
