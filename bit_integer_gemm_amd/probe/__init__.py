@@ -22,6 +22,10 @@ its own MFMAs: how many unpack instructions fit between a wave's MFMAs.
 their MFMAs (one wave per SIMD; copies in all four waves or in one): the cost
 of a copy to its wave, and where the CU's copy path saturates.
 
+6. The 1-bit GEMM on the vector ALUs (AND + popcount-add per pair of 32-bit
+words) at 4096 x 4096 x 8192 bits, against the vector ALUs' peak and against
+the library's 1-bit GEMM on the same operands (identical results required).
+
   python -m bit_integer_gemm_amd.probe          # prints one JSON object
 """
 from __future__ import annotations
@@ -196,8 +200,70 @@ def measure_copies(iters: int = 500) -> dict:
     return out
 
 
+VALU_B1_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 2 * 64 / 1e12   # and + popcount-add per 32 bit-MACs
+
+
+def valu_b1(A, B, C, reps: int = 1) -> float:
+    """C = popcount(A AND B) over K bits on the vector ALUs (A: M x K/32, B: N x
+    K/32 int32 tensors holding the bit words, C: M x N int32); milliseconds for
+    `reps` launches."""
+    lib = ctypes.CDLL(LIB)
+    lib.valu_b1_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_int]
+    lib.valu_b1_run.restype = ctypes.c_float
+    M, kw = A.shape
+    N = B.shape[0]
+    ms = lib.valu_b1_run(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, 32 * kw, reps)
+    if ms < 0:
+        raise RuntimeError(f"valu_b1_run failed ({ms})")
+    return ms
+
+
+def measure_valu_b1(M: int = 4096, N: int = 4096, K: int = 8192) -> dict:
+    """The vector-ALU popcount 1-bit GEMM against the library's 1-bit GEMM
+    (automatic choice: the FP4 matrix-core route) on the same operands; the
+    two results must be identical."""
+    import torch
+    import bit_integer_gemm_amd as lb
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    A = torch.randint(-2**31, 2**31 - 1, (M, K // 32), dtype=torch.int32, device="cuda", generator=g)
+    B = torch.randint(-2**31, 2**31 - 1, (N, K // 32), dtype=torch.int32, device="cuda", generator=g)
+    Cv = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    Cl = torch.empty_like(Cv)
+    valu_b1(A, B, Cv)
+    lb.lb_gemm_b1(A, B, Cl)
+    torch.cuda.synchronize()
+    if not torch.equal(Cv, Cl):
+        raise RuntimeError("the vector-ALU 1-bit GEMM and the library disagree")
+    ops = 2.0 * M * N * K
+    reps = 20
+    valu_b1(A, B, Cv, 3)
+    t_valu = min(valu_b1(A, B, Cv, reps) for _ in range(3)) / reps * 1e-3
+    for _ in range(10):
+        lb.lb_gemm_b1(A, B, Cl)
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            lb.lb_gemm_b1(A, B, Cl)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        best = t if best is None else min(best, t)
+    out = {"shape": [M, N, K], "valu_us": round(t_valu * 1e6, 2), "valu_tops": round(ops / t_valu / 1e12, 1),
+           "valu_frac_of_valu_peak": round(ops / t_valu / 1e12 / VALU_B1_PEAK_TOPS, 3),
+           "library_us": round(best * 1e6, 2), "library_tops": round(ops / best / 1e12, 1),
+           "library_speedup": round(t_valu / best, 2), "identical": True}
+    print(f"[probe] 1-bit on the vector ALUs: {out['valu_us']} us, {out['valu_tops']} TOP/s "
+          f"({out['valu_frac_of_valu_peak']:.0%} of {VALU_B1_PEAK_TOPS:.1f}); library {out['library_us']} us "
+          f"({out['library_speedup']}x)", flush=True)
+    return out
+
+
 def main():
     if not os.path.exists(LIB):
         sys.exit(f"{LIB} not built: run __graft_entry__.build() or bit_integer_gemm_amd.probe.build()")
     print(json.dumps({"mfma": measure(), "mix": measure_mix(), "stores": measure_stores(),
-                      "slots": measure_slots(), "copies": measure_copies()}))
+                      "slots": measure_slots(), "copies": measure_copies(), "valu_b1": measure_valu_b1()}))

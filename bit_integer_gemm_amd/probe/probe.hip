@@ -24,6 +24,12 @@
 // copies (16 bytes per lane) between its MFMAs, B copies after every CPM-th
 // MFMA, in all four waves of a workgroup or in wave 0 only: the cost of a copy
 // to its wave, and the CU's copy bandwidth once copies collide.
+//
+// 6. (below) The 1-bit GEMM on the vector ALUs, the form the scope of the
+// 1-bit product starts from: each thread owns an 8 x 8 block of C and adds
+// popcount(a AND b) of 32-bit words (one v_and_b32 and one v_bcnt_u32_b32 per
+// word pair, 64 bit-MACs).  Its rate against the vector ALUs' peak, and
+// against the library's matrix-core route, measured on the same shape.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -267,7 +273,107 @@ __global__ __launch_bounds__(256) void copy_kernel(const char *src, uint32_t src
     if (lane == 0) cyc[gid / 64u] = (uint32_t)(t1 - t0);
 }
 
+// 6. C (M x N int32) = popcount(A AND B) summed over K bits; A is M x Kw and B
+// N x Kw words (row-major, K-contiguous).  A 128 x 128 tile per workgroup of
+// 256 threads, each thread rows 8*ty.. and columns 8*tx.. (tx = t % 16, ty =
+// t / 16).  A stage holds 16 words of K for the tile's 128 A rows and 128 B
+// rows in LDS, word-major (S[w][row]) so that a thread's 8 words of one K word
+// are two 16-byte reads (B: 16 threads of a wave read 128 consecutive words;
+// A: broadcast).  Thread t copies row t (A for t < 128, B after) through
+// registers: the next stage is loaded before the current one's arithmetic
+// and written to the other LDS buffer after it.  Requires Kw % 16 == 0 (the
+// host checks); rows past M or N read as zero and are not stored.
+constexpr int VB_KW = 16;
+__global__ __launch_bounds__(256) void valu_b1_kernel(const uint32_t *__restrict__ A, const uint32_t *__restrict__ B,
+                                                      int32_t *__restrict__ C, int M, int N, int Kw, int tiles_n)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t S[2][VB_KW][256];   // [buf][word][A rows 0..127, B rows 128..255]
+    const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+    const int m0 = (blockIdx.x / tiles_n) * 128, n0 = (blockIdx.x % tiles_n) * 128;
+    const int row = t < 128 ? m0 + t : n0 + (t - 128);
+    const bool live = t < 128 ? row < M : row < N;
+    const uint32_t *src = (t < 128 ? A : B) + (int64_t)(live ? row : 0) * Kw;
+    uint32_t acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0;
+    uint4 st[VB_KW / 4];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < VB_KW / 4; ++q)
+            st[q] = live ? *(const uint4 *)(src + k0 + 4 * q) : make_uint4(0, 0, 0, 0);
+    };
+    auto put = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < VB_KW / 4; ++q) {
+            S[buf][4 * q + 0][t] = st[q].x;
+            S[buf][4 * q + 1][t] = st[q].y;
+            S[buf][4 * q + 2][t] = st[q].z;
+            S[buf][4 * q + 3][t] = st[q].w;
+        }
+    };
+    const int nst = Kw / VB_KW;
+    load(0);
+    put(0);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nst) load((s + 1) * VB_KW);
+#pragma unroll 4
+        for (int w = 0; w < VB_KW; ++w) {
+            const uint4 a0 = *(const uint4 *)&S[buf][w][8 * ty], a1 = *(const uint4 *)&S[buf][w][8 * ty + 4];
+            const uint4 b0 = *(const uint4 *)&S[buf][w][128 + 8 * tx], b1 = *(const uint4 *)&S[buf][w][128 + 8 * tx + 4];
+            const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const uint32_t b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    // popcount-and-add in one instruction (as written, the
+                    // compiler regroups the sums into three-input adds)
+                    const uint32_t x = a[i] & b[j];
+                    asm volatile("v_bcnt_u32_b32 %0, %1, %0" : "+v"(acc[i][j]) : "v"(x));
+                }
+        }
+        if (s + 1 < nst) put(buf ^ 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int m = m0 + 8 * ty + i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int n = n0 + 8 * tx + j;
+            if (n < N) C[(int64_t)m * N + n] = (int32_t)acc[i][j];
+        }
+    }
+}
+
 extern "C" {
+
+// 6. C = popcount(A AND B) GEMM on the vector ALUs (M x N, K bits with K % 512
+// == 0); runs `reps` launches and returns the milliseconds between HIP events
+// around them, or < 0 on a bad shape or a HIP error.
+float valu_b1_run(const uint32_t *A, const uint32_t *B, int32_t *C, int M, int N, int K, int reps)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || K % (32 * VB_KW) != 0 || reps <= 0) return -5.f;
+    const int tiles_n = (N + 127) / 128;
+    const int blocks = ((M + 127) / 128) * tiles_n;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1.f;
+    (void)hipEventRecord(e0, 0);
+    for (int r = 0; r < reps; ++r)
+        hipLaunchKernelGGL(valu_b1_kernel, dim3(blocks), dim3(256), 0, 0, A, B, C, M, N, K / 32, tiles_n);
+    (void)hipEventRecord(e1, 0);
+    if (hipEventSynchronize(e1) != hipSuccess) return -3.f;
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return hipGetLastError() == hipSuccess ? ms : -4.f;
+}
 
 // Launch `blocks` workgroups of slot_kernel<op, v>; cyc holds blocks * 4
 // words, out blocks * 256 floats.  0 on success, < 0 on a HIP error or an

@@ -228,6 +228,21 @@ def test_b1_at_max_k(variant):
     assert (run("b1", fives, fives[:N], variant) == K // 2).all()
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 300, 1024), (128, 128, 512), (1, 257, 2048), (333, 64, 8192)])
+def test_probe_valu_b1_matches_oracle(M, N, K):
+    """The vector-ALU popcount 1-bit GEMM of the probe module (the measured
+    baseline the matrix-core routes replace) is exact against the oracle on
+    ragged shapes."""
+    from bit_integer_gemm_amd import probe
+    if not os.path.exists(probe.LIB):
+        pytest.fail(f"{probe.LIB} not built: run __graft_entry__.build()")
+    A, B = inputs.b1_rows(M, K, 71), inputs.b1_rows(N, K, 72)
+    C = torch.full((M, N), 7, dtype=torch.int32, device="cuda")
+    probe.valu_b1(to_dev(A.view(np.int32)), to_dev(B.view(np.int32)), C)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(C.cpu().numpy(), oracle.gemm_b1(A, B, K))
+
+
 def test_b1_equals_int8_gemm_of_unpacked_bits():
     """The 1-bit route against the int8 route on the GPU: unpacking the bits to
     0/1 bytes and running the int8 GEMM must give the same C, for K values that
