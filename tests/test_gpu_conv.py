@@ -172,6 +172,45 @@ def test_conv_layer_full_compare(kind, name):
     np.testing.assert_array_equal(got, want, err_msg=f"{kind} {name}")
 
 
+def test_conv_graph_capture_replays_match_eager():
+    """Automatic-choice convolutions (a few-channel layer, which takes the small
+    tile, and a wider one) captured into a HIP graph: every replay, with eager
+    work in between, reproduces the oracle's result."""
+    cases = [("s8", (2, 11, 9, 16, 48, 3, 3, (1, 1), (1, 1))), ("s4", (1, 8, 7, 128, 96, 3, 3, (2, 1), (1, 1)))]
+    outs, wants = [], []
+    g = torch.cuda.CUDAGraph()
+    ops = []
+    for kind, (N, H, W, C, Co, Kh, Kw, st, pd) in cases:
+        x, f = make(kind, N, H, W, C, Co, Kh, Kw, 990)
+        wants.append(ref(kind, x, f, C, st, pd))
+        Ho, Wo = lb.conv_out_dims(H, W, Kh, Kw, st, pd)
+        Y = torch.zeros((N, Ho, Wo, Co), dtype=torch.int32, device="cuda")
+        ops.append((kind, to_dev(x), to_dev(f), Y, st, pd))
+        outs.append(Y)
+    fn = {"s8": lb.lb_conv2d_s8, "s4": lb.lb_conv2d_s4}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for kind, X, F, Y, st, pd in ops:
+            fn[kind](X, F, Y, st, pd, lb.LB_AUTO)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for kind, X, F, Y, st, pd in ops:
+            fn[kind](X, F, Y, st, pd, lb.LB_AUTO)
+    for r in range(3):
+        for Y in outs:
+            Y.fill_(-1)
+        kind, X, F, Y, st, pd = ops[0]
+        scratch = torch.empty_like(Y)
+        fn[kind](X, F, scratch, st, pd, 3)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for Y, want in zip(outs, wants):
+            np.testing.assert_array_equal(Y.cpu().numpy(), want, err_msg=f"replay {r}")
+
+
 def test_conv_extreme_values():
     """All -128 operands with padding: every output is 16384*C times its in-image tap count."""
     N, H, W, C, Co, Kh, Kw, st, pd = 1, 6, 7, 64, 20, 3, 3, (1, 2), (1, 1)
