@@ -478,6 +478,23 @@ def test_linear_full_size_exact():
     assert_rel(out, oracle.linear_s8(X, W, sx, sw))
 
 
+def test_linear_large_ragged_sampled():
+    """A linear layer of ragged size with a K tail, 8000 x 11000 x 4000: the
+    automatic path splits it into whole rounds of large tiles and a remainder,
+    with partial edge tiles and a short last K stage.  Whole sampled rows and
+    columns (first, last and four random of each) against the oracle."""
+    M, N, K = 8000, 11000, 4000
+    print("[parity] linear ragged 8000x11000x4000", flush=True)
+    X, W = inputs.s8_rows(M, K, 5101), inputs.s8_rows(N, K, 5102)
+    sx, sw = inputs.scales(M, 5103), inputs.scales(N, 5104)
+    out = run_linear(X, W, sx, sw, lb.LB_AUTO)
+    rng = inputs.rng(5105)
+    rows = sorted({0, M - 1, *rng.integers(0, M, 4).tolist()})
+    cols = sorted({0, N - 1, *rng.integers(0, N, 4).tolist()})
+    assert_rel(out[rows], oracle.linear_s8(X[rows], W, sx[rows], sw))
+    assert_rel(out[:, cols], oracle.linear_s8(X, W[cols], sx, sw[cols]))
+
+
 def test_graph_capture_replays_match_eager():
     """The library's launches are captured into a HIP graph (the sweep times
     short kernels that way); every replay, with eager work in between, must
