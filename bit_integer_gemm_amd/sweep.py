@@ -18,7 +18,10 @@ labels: the fastest variant, where every variant within EPS of the fastest
 counts as tied and a tie goes to the default variant, else to the lowest index
 (timing noise on short kernels must not make the selected variant slower than
 the default, nor flip labels between near-equal variants), and writes
-csrc/selector_table.inc.
+csrc/selector_table.inc: each grid shape's label and runner-up, and its nine
+times over the fastest in thousandths (from which the library's table mode
+takes, for a shape off the grid, the variant with the best worst case over the
+grid shapes that bracket it).
 
 Inputs: for each K, one seeded uniform operand pair of the largest M and N is
 drawn (int8 over [-128, 127], int4 over [-8, 7], Bernoulli(0.5) bits) and each
