@@ -266,6 +266,33 @@ def test_repeated_queries_and_mode_switches_agree():
     assert any(table[s] != net[s] for s in shapes)
 
 
+def test_concurrent_queries_from_threads_agree():
+    """Selection is safe to call from several threads at once: each thread keeps
+    its own remembered answers, and every answer equals a single-threaded
+    query of the same shape."""
+    import random
+    import threading
+    rnd = random.Random(11)
+    shapes = [(rnd.randrange(3), rnd.randint(1, 20000), rnd.randint(1, 20000), 128 * rnd.randint(1, 256))
+              for _ in range(300)]
+    want = {s: lb.lb_select_variant(*s, 256) for s in shapes}
+    bad = []
+
+    def worker(seed):
+        r = random.Random(seed)
+        for _ in range(2000):
+            s = shapes[r.randrange(len(shapes))]
+            got = lb.lb_select_variant(*s, 256)
+            if got != want[s]:
+                bad.append((s, got, want[s]))
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:5]
+
+
 def test_sweep_records_of_the_automatic_path(tmp_path):
     """Sweep files may hold records of the library's own choice (variant
     "auto"): labels ignore them, and the evaluation reports the automatic path
