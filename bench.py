@@ -305,7 +305,29 @@ def measure(workload, torch, lb):
         res.update({"int8_route_us": round(t_int8_route * 1e6, 2),
                     "fp4_route_speedup_vs_int8_route": round(t_int8_route / t_auto, 4),
                     "int8_route_frac_of_int8_peak": round(ops / t_int8_route / 1e12 / PEAK_INT8_TOPS, 4)})
+        res.update(valu_b1_baseline(ops_, out, ops, t_auto, torch))
     return res
+
+
+def valu_b1_baseline(ops_, out, ops, t_auto, torch):
+    """The 1-bit GEMM on the vector ALUs (AND + popcount-add; the probe
+    module's kernel, not part of the library) on the same operands: its time,
+    its fraction of the vector-ALU peak, and whether its C equals the
+    library's.  Empty when the probe library is not built."""
+    from bit_integer_gemm_amd import probe
+    if not os.path.exists(probe.LIB):
+        return {"valu_popcount_note": "probe library not built"}
+    A, B = ops_
+    C = torch.empty_like(out)
+    probe.valu_b1(A, B, C)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(C, out))
+    reps = 20
+    probe.valu_b1(A, B, C, 3)
+    t = min(probe.valu_b1(A, B, C, reps) for _ in range(3)) / reps * 1e-3
+    return {"valu_popcount_us": round(t * 1e6, 2), "valu_popcount_tops": round(ops / t / 1e12, 1),
+            "valu_popcount_frac_of_valu_peak": round(ops / t / 1e12 / probe.VALU_B1_PEAK_TOPS, 4),
+            "speedup_vs_valu_popcount": round(t / t_auto, 3), "valu_popcount_identical": same}
 
 
 def time_cold(fn, torch, reps=15, flush_mib=512):
