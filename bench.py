@@ -12,7 +12,8 @@ Prints ONE JSON line with the throughput in TOPS (2*M*N*K per GEMM), the
 roofline of the GEMM kernel against MI355X's dense int8 MFMA peak, and the CPU
 oracle timed on a bounded sample of the same workload.  Extra fields report the
 int4 and int8 GEMMs at 4096^3, the 1-bit GEMM at 4096 x 4096 x 8192 bits and the
-int8 linear layer, each with its selected and default variants (kernel time from
+int8 linear layer (whole, and one GPU's share of it split eight ways by columns
+or by rows), each with its selected and default variants (kernel time from
 HIP-graph replays, so that host launch cost is excluded), and, as context, the
 vendor library's int8 GEMM (hipBLASLt via torch._int_mm) at the same sizes; and
 four low-bit convolution layers with their roofline and the time of the dense
@@ -54,6 +55,10 @@ WORKLOADS = {
     "b1_gemm_4096x4096x8192": ("b1", 4096, 4096, 8192, (3001, 3002)),
     "s8_linear_8192x11008x4096": ("linear", 8192, 11008, 4096, (5001, 5002, 5003, 5004)),
     "s8_gemm_256": ("s8", 256, 256, 256, (1001, 1002)),
+    # one GPU's share of the linear layer split over 8 GPUs, by columns of W
+    # (and the output) and by rows of X: the shapes each GPU would run
+    "s8_linear_colshard8_8192x1376x4096": ("linear", 8192, 1376, 4096, (5001, 5002, 5003, 5004)),
+    "s8_linear_rowshard8_1024x11008x4096": ("linear", 1024, 11008, 4096, (5001, 5002, 5003, 5004)),
 }
 
 # Convolution layers (synthetic NHWC batches; shapes of common CNN stages, not
@@ -489,7 +494,7 @@ def main():
     if not args.only and not args.no_extras:
         extras = {}
         for w in ("s4_gemm_4096", "s8_gemm_4096", "b1_gemm_4096x4096x8192", "s8_linear_8192x11008x4096",
-                  "s8_gemm_256"):
+                  "s8_linear_colshard8_8192x1376x4096", "s8_linear_rowshard8_1024x11008x4096", "s8_gemm_256"):
             extras[w] = measure(w, torch, lb)
         for w in CONV_LAYERS:
             extras[w] = measure_conv(w, torch, lb)

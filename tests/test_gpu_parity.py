@@ -495,6 +495,21 @@ def test_linear_large_ragged_sampled():
     assert_rel(out[:, cols], oracle.linear_s8(X, W[cols], sx, sw[cols]))
 
 
+@pytest.mark.parametrize("M,N", [(8192, 1376), (1024, 11008)])
+def test_linear_shard_of_eight_exact(M, N):
+    """One GPU's share of the linear layer split over eight GPUs, by columns of
+    W (8192 x 1376 x 4096) or by rows of X (1024 x 11008 x 4096), with the
+    automatic variant: every output against the oracle within the relative
+    bound."""
+    K = 4096
+    s = inputs.SEEDS["linear"]
+    print(f"[parity] linear shard {M}x{N}x{K}", flush=True)
+    X, W = inputs.s8_rows(M, K, s[0]), inputs.s8_rows(N, K, s[1])
+    sx, sw = inputs.scales(M, s[2]), inputs.scales(N, s[3])
+    out = run_linear(X, W, sx, sw, lb.LB_AUTO)
+    assert_rel(out, oracle.linear_s8(X, W, sx, sw))
+
+
 def test_graph_capture_replays_match_eager():
     """The library's launches are captured into a HIP graph (the sweep times
     short kernels that way); every replay, with eager work in between, must
