@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "liblbgemm.so")
 
 LB_OK, LB_ERR_NULL, LB_ERR_SHAPE, LB_ERR_ALIGN, LB_ERR_VARIANT, LB_ERR_OVERFLOW, LB_ERR_HIP = range(7)
 LB_S8, LB_S4, LB_B1 = 0, 1, 2
+LB_PLAN_LINEAR = 3   # lb_auto_plan's op code for the linear layer
 LB_AUTO = -1
 LB_NUM_VARIANTS = 9
 LB_DEFAULT_VARIANT = 7
@@ -40,7 +41,7 @@ CONV_C_ALIGN = {LB_S8: 16, LB_S4: 32}
 # Exported symbols of include/lb_gemm.h (checked by the CPU tests).
 EXPORTS = ("lb_gemm_s8", "lb_gemm_s4", "lb_gemm_b1", "lb_gemm_s8_linear", "lb_conv2d_s8",
            "lb_conv2d_s4", "lb_select_variant", "lb_status_string", "lb_variant_info",
-           "lb_build_id")
+           "lb_build_id", "lb_auto_plan")
 
 
 class LbError(RuntimeError):
@@ -87,6 +88,8 @@ def load(path: str = LIB_PATH):
     lib.lb_status_string.restype = ctypes.c_char_p
     lib.lb_variant_info.argtypes = [i32, i32, ip, ip, ip, ip]
     lib.lb_variant_info.restype = i32
+    lib.lb_auto_plan.argtypes = [i32, i64, i64, i64, ip, ip, ip, ip]
+    lib.lb_auto_plan.restype = i32
     _lib = lib
     return lib
 
@@ -243,6 +246,15 @@ def lb_variant_info(dtype: int, variant: int) -> dict:
     vals = [ctypes.c_int(0) for _ in range(4)]
     _raise(load().lb_variant_info(dtype, variant, *[ctypes.byref(v) for v in vals]), "lb_variant_info")
     return dict(zip(("tile_m", "tile_n", "tile_k", "stages"), (v.value for v in vals)))
+
+
+def lb_auto_plan(op: int, M: int, N: int, K: int) -> dict:
+    """What an LB_AUTO call makes for a shape on the current device: the number
+    of launches, the first launch's workgroup tile and its K bands.  op: LB_S8,
+    LB_S4, LB_B1 or LB_PLAN_LINEAR."""
+    vals = [ctypes.c_int(0) for _ in range(4)]
+    _raise(load().lb_auto_plan(op, M, N, K, *[ctypes.byref(v) for v in vals]), "lb_auto_plan")
+    return dict(zip(("launches", "tile_m", "tile_n", "k_bands"), (v.value for v in vals)))
 
 
 def ops(dtype: int, M: int, N: int, K: int) -> int:

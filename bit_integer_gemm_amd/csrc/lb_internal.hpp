@@ -11,6 +11,11 @@ namespace lb {
 // per block, fp32 accumulation exact below 2^24).
 enum { KIND_S8 = 0, KIND_S4 = 1, KIND_LINEAR = 2, KIND_B1 = 3, KIND_B1F4 = 4 };
 
+// Internal tile codes beside the nine public variants (never accepted from a
+// caller): the four-wave kernel on 256x192 and 192x256 tiles, for the int8
+// GEMM and the linear layer.
+enum { W4_256x192 = 16, W4_192x256 = 17 };
+
 // int8 MFMA family (int8 GEMM, packed-int4 GEMM, int8 linear layer, and the
 // 1-bit GEMM on weighted bit planes).  Kb is the row length of A and B in
 // bytes (K for int8, K/2 for int4, K/8 for 1-bit); ldo is the distance in

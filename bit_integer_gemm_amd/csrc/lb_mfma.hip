@@ -683,14 +683,39 @@ __device__ inline void mfma_tied(i32x4 &c, i32x4 a, i32x4 b)
     asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
-template <int KIND>
+// Item of a spread schedule at MFMA slot s: H items over S slots (S >= H),
+// item c at slot floor(c*S/H) (OFF = 0) or floor((c+1)*S/H) - 1 (OFF = 1);
+// -1 if no item falls on s.
+template <int S, int H, int OFF>
+__device__ constexpr int spread_item(int s)
+{
+    for (int c = 0; c < H; ++c)
+        if (((c + OFF) * S) / H - OFF == s) return c;
+    return -1;
+}
+
+// FM x FN: fragment rows and columns of a wave's sub-tile (16 x 16 each); the
+// workgroup tile is (32*FM) x (32*FN).  8 x 8 (256x256) serves every type;
+// 8 x 6 (256x192) and 6 x 8 (192x256) serve the int8 GEMM and the linear layer
+// when a product's 256x256 tiles would fill less than one round of the CUs
+// (the host picks them for an automatic choice).  The copies and the next
+// block's fragment reads are spread over a half-block's MFMA slots by
+// spread_item; for 8 x 8 that is the fixed pattern of one copy per four slots
+// and one read per two.
+template <int KIND, int FM, int FN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mfma_w4_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, void *__restrict__ out,
     const float *__restrict__ sx, const float *__restrict__ sw,
     int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n, int32_t ldo, int32_t ksplit)
 {
-    constexpr int FM = 8, FN = 8, SS = 64 * 1024;
-    constexpr int SCALE_BYTES = KIND == KIND_LINEAR ? 2 * 256 * 4 : 0;
+    static_assert(FM % 2 == 0 && FM >= 4 && FM <= 8 && FN % 2 == 0 && FN >= 4 && FN <= 8, "wave sub-tile");
+    static_assert((FM == 8 && FN == 8) || KIND == KIND_S8 || KIND == KIND_LINEAR,
+                  "int4 and 1-bit run the 256x256 tile only");
+    constexpr int BM = 32 * FM, BN = 32 * FN;
+    constexpr int SS = (BM + BN) * 128;   // one super-stage: 128 K-bytes of A and B
+    constexpr int BOFF = BM * 128;        // B's blocks within a super-stage
+    constexpr int NCP = FM + FN;          // refill copies per wave per super-stage
+    constexpr int SCALE_BYTES = KIND == KIND_LINEAR ? (BM + BN) * 4 : 0;
     __shared__ __attribute__((aligned(1024))) char smem[2 * SS + SCALE_BYTES];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -714,7 +739,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     } else {
         tile_of_block(blockIdx.x, tiles_m, tiles_n, 4u, tm, tn);
     }
-    const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
     // Split K as in the other kernels: row blockIdx.y of the grid sums K bytes
     // [kbeg, kbeg + klen) and adds its partial sums into a zeroed C.
@@ -726,10 +751,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t a_bytes = (int64_t)(M - m0) * Kb - kbeg;
     const int64_t b_bytes = (int64_t)(N - n0) * Kb - kbeg;
 
-    // Copy q (0..7 per operand) of wave w fills half u%2 of block u/2, u = w + 4q.
-    uint32_t voff[8];
+    // Copy q (0..FM-1 for A, 0..FN-1 for B) of wave w fills half u%2 of block
+    // u/2, u = w + 4q.
+    constexpr int NV = FM > FN ? FM : FN;
+    uint32_t voff[NV];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NV; ++q) {
         const int u = (int)wave + 4 * q;
         voff[q] = (uint32_t)((u / 2) * 16 + (u % 2) * 8 + (int)(lane >> 3)) * (uint32_t)Kb +
                   wide_chunk_of_lane(lane) * 16u;
@@ -744,13 +771,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         return make_rsrc(Bb + k0, b_bytes > k0 ? (uint64_t)(b_bytes - k0) : 0);
     };
     auto copy_q = [&](const i32x4 &ra, const i32x4 &rb, uint32_t sbase, int q) {
-        if (q < 8) dma16(ra, voff[q], sbase + ((int)wave + 4 * q) * 1024);
-        else dma16(rb, voff[q - 8], sbase + 32768 + ((int)wave + 4 * (q - 8)) * 1024);
+        if (q < FM) dma16(ra, voff[q], sbase + ((int)wave + 4 * q) * 1024);
+        else dma16(rb, voff[q - FM], sbase + BOFF + ((int)wave + 4 * (q - FM)) * 1024);
     };
     // A pieces past the band's K are zeroed once their super-stage has landed.
     auto zero_tail = [&](int slot, int64_t k0) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < FM; ++q) {
             const int u = (int)wave + 4 * q;
             if (k0 + (int)wide_chunk_of_lane(lane) * 16 >= klen)
                 *(i32x4 *)(smem + slot * SS + u * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
@@ -768,7 +795,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int nss = (klen + 127) / 128;  // super-stages
     const int nk = (klen + 63) / 64;     // 64-byte blocks
     const bool k_tail = (klen % 128) != 0;
-    // Linear layer: wave 0 copies sx[m0 .. m0+256) and sw[n0 .. n0+256) into LDS
+    // Linear layer: wave 0 copies sx[m0 .. m0+BM) and sw[n0 .. n0+BN) into LDS
     // before the first super-stage (entries past M or N read as zero); the first
     // stage wait covers these older copies, and the epilogue reads the scales
     // from LDS (read from global memory at the end of the tile, they made the
@@ -779,21 +806,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const i32x4 rx = make_rsrc(sx + m0, (uint64_t)(M - m0) * 4);
             const i32x4 rw = make_rsrc(sw + n0, (uint64_t)(N - n0) * 4);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dma4(rx, lane * 4 + q * 256, sbase + q * 256);
+            for (int q = 0; q < BM / 64; ++q) dma4(rx, lane * 4 + q * 256, sbase + q * 256);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dma4(rw, lane * 4 + q * 256, sbase + 1024 + q * 256);
+            for (int q = 0; q < BN / 64; ++q) dma4(rw, lane * 4 + q * 256, sbase + BM * 4 + q * 256);
         }
     }
     {
         const i32x4 ra = rsrc_a(0), rb = rsrc_b(0);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) copy_q(ra, rb, smem_base, q);
+        for (int q = 0; q < NCP; ++q) copy_q(ra, rb, smem_base, q);
     }
     if (nss > 1) {
         const i32x4 ra = rsrc_a(1), rb = rsrc_b(1);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) copy_q(ra, rb, smem_base + SS, q);
-        wait_vm_barrier<16>();
+        for (int q = 0; q < NCP; ++q) copy_q(ra, rb, smem_base + SS, q);
+        wait_vm_barrier<NCP>();
     } else {
         wait_vm_barrier<0>();
     }
@@ -817,7 +844,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa0[i] = *(const i32x4 *)(f + (wm * FM + i) * 2048);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb0[j] = *(const i32x4 *)(f + 32768 + (wn * FN + j) * 2048);
+        for (int j = 0; j < FN; ++j) fb0[j] = *(const i32x4 *)(f + BOFF + (wn * FN + j) * 2048);
     }
 
     // Refill of the slot released at the last odd block's barrier (no refill
@@ -828,27 +855,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     uint32_t csb = smem_base;
     auto copy_r = [&](int q) { copy_q(cra, crb, csb, q); };
 
-    // MFMAs of fragment rows i0 .. i0+3 (int8).  CP: issue refill copies
-    // (eight, two per row): copies 8-15 in an even block's first half, 0-7 in
-    // an odd block's second half.  The second half also reads the next
-    // block's fragments from f, four per row.
+    // MFMAs of fragment rows i0 .. i0+FM/2-1 (int8).  CP: issue refill copies,
+    // NCP/2 spread evenly over the half's FM/2 x FN MFMA slots: copies
+    // NCP/2.. in an even block's first half, 0..NCP/2-1 in an odd block's
+    // second half (8 x 8: one per four slots).  The second half also reads
+    // the next block's FM + FN fragments from f, B first, spread likewise
+    // (8 x 8: one per two slots).
     auto half = [&](auto cp_c, const i32x4 *fa, const i32x4 *fb, int i0, bool second, const char *f,
                     i32x4 *na, i32x4 *nb) {
         constexpr bool CP = decltype(cp_c)::value;
+        constexpr int S = FM / 2 * FN, H = NCP / 2;
 #pragma unroll
         for (int i = i0; i < i0 + FM / 2; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
+                const int sl = (i - i0) * FN + j;
                 mfma_tied(acc[i][j], fb[j], fa[i]);
                 if (LB_AB_COPY_BURST) {
-                    if (CP && second && j % 2 == 0) copy_r((i - i0) * 4 + j / 2);
-                } else if (CP && j % 4 == 0) {
-                    copy_r((second ? 0 : 8) + (i - i0) * 2 + j / 4);
+                    const int c = spread_item<S, NCP, 0>(sl);
+                    if (CP && second && c >= 0) copy_r(c);
+                } else if (CP) {
+                    const int c = spread_item<S, H, 0>(sl);
+                    if (c >= 0) copy_r((second ? 0 : H) + c);
                 }
-                if (second && j % 2 == 1) {
-                    const int q = (i - i0) * 4 + j / 2;  // 0..15
-                    if (q < FN) nb[q] = *(const i32x4 *)(f + 32768 + (wn * FN + q) * 2048);
-                    else na[q - FN] = *(const i32x4 *)(f + (wm * FM + q - FN) * 2048);
+                if (second) {
+                    const int q = spread_item<S, FM + FN, 1>(sl);
+                    if (q >= 0 && q < FN) nb[q] = *(const i32x4 *)(f + BOFF + (wn * FN + q) * 2048);
+                    else if (q >= FN) na[q - FN] = *(const i32x4 *)(f + (wm * FM + q - FN) * 2048);
                 }
             }
     };
@@ -880,7 +913,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto copy_r4 = [&](int q) {
         if (q % 8 == 0) vcur = voff[0];
         dma16(q < 8 ? cra : crb, vcur,
-              csb + (q < 8 ? 0u : 32768u) + ((uint32_t)wave + 4u * (uint32_t)(q % 8)) * 1024u);
+              csb + (q < 8 ? 0u : (uint32_t)BOFF) + ((uint32_t)wave + 4u * (uint32_t)(q % 8)) * 1024u);
         asm volatile("v_add_u32 %0, %1, %0" : "+v"(vcur) : "s"(kstride));
     };
     using P0 = std::integral_constant<int, 0>;
@@ -981,7 +1014,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     const bool cp = second ? P == 1 : (P == 0 && !FIRST);
                     if (cp && sl % FN == 0) copy_r4((second ? 0 : 8) + (i % (FM / 2)) * 2 + sl / FN);
                     const int z = (i - FM / 2) * 2 * FN + sl;  // slot in the second half
-                    if (second && z < FN) bhi4[Q][z] = *(const i32x4 *)(f + 32768 + (wn * FN + z) * 2048);
+                    if (second && z < FN) bhi4[Q][z] = *(const i32x4 *)(f + BOFF + (wn * FN + z) * 2048);
                     // the next block's A fragment q replaces fragment q once
                     // this block's planes of row q are made: q <= 4 in row 4,
                     // later ones in their own row, at slots 8-12
@@ -1110,7 +1143,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     if (cp && j == 0 && r % 2 == 0) copy_r4((H == 1 ? 0 : 8) + (r % (2 * FM)) / 2);
                     if (p == 3) {
                         // plane 3: the next block's fragments
-                        if (i == 0) fb[j] = *(const i32x4 *)(f + 32768 + (wn * FN + j) * 2048);
+                        if (i == 0) fb[j] = *(const i32x4 *)(f + BOFF + (wn * FN + j) * 2048);
                         if (j == 6) fa[i] = *(const i32x4 *)(f + (wm * FM + i) * 2048);
                     }
                     // A plane of the next row: slots 1 ..
@@ -1153,15 +1186,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        const int64_t m = m0 + wm * 128 + i * 16 + (lane % 16);
+        const int64_t m = m0 + wm * (16 * FM) + i * 16 + (lane % 16);
         if (m >= M) continue;
         const float *lds_sx = (const float *)(smem + 2 * SS);
-        const float *lds_sw = lds_sx + 256;
+        const float *lds_sw = lds_sx + BM;
         float scale_m = 0.f;
         if constexpr (KIND == KIND_LINEAR) scale_m = lds_sx[m - m0];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * 128 + j * 16 + (lane / 16) * 4;
+            const int64_t n = n0 + wn * (16 * FN) + j * 16 + (lane / 16) * 4;
             if (n >= N) continue;
             i32x4 v;
             if constexpr (KIND == KIND_B1F4) {
@@ -1198,16 +1231,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
-template <int KIND>
+template <int KIND, int FM, int FN>
 static hipError_t launch_w4(const void *A, const void *B, void *out, const float *sx, const float *sw,
                             int64_t M, int64_t N, int64_t Kb, int64_t ldo, int64_t ksplit, hipStream_t s)
 {
-    const uint64_t tm = (uint64_t)((M + 255) / 256), tn = (uint64_t)((N + 255) / 256);
+    constexpr int64_t BM = 32 * FM, BN = 32 * FN;
+    const uint64_t tm = (uint64_t)((M + BM - 1) / BM), tn = (uint64_t)((N + BN - 1) / BN);
     if (tm * tn > 0x7FFFFFFFull) return hipErrorInvalidValue;
     if (ksplit <= 0 || ksplit > Kb) ksplit = Kb;
     if (ksplit < Kb && (KIND == KIND_LINEAR || ksplit % 128 != 0)) return hipErrorInvalidValue;
     const uint32_t nsplit = (uint32_t)((Kb + ksplit - 1) / ksplit);
-    hipLaunchKernelGGL((mfma_w4_kernel<KIND>), dim3((uint32_t)(tm * tn), nsplit), dim3(256), 0, s,
+    hipLaunchKernelGGL((mfma_w4_kernel<KIND, FM, FN>), dim3((uint32_t)(tm * tn), nsplit), dim3(256), 0, s,
                        (const int8_t *)A, (const int8_t *)B, out, sx, sw, (int32_t)M, (int32_t)N,
                        (int32_t)Kb, (uint32_t)tm, (uint32_t)tn, (int32_t)ldo, (int32_t)ksplit);
     return hipGetLastError();
@@ -1302,11 +1336,19 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
         // four-wave kernel to int8: 8 waves of 64x128.
         if constexpr ((KIND == KIND_S8 || KIND == KIND_LINEAR ||
                        ((KIND == KIND_S4 || KIND == KIND_B1F4) && !LB_AB_W4_INT8_ONLY)) && !CONV)
-            return launch_w4<KIND>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
+            return launch_w4<KIND, 8, 8>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
         else
             return launch_one<std::conditional_t<b1 || (KIND == KIND_S4 && !CONV), L2W8, L2W16>, KIND, CONV>(
                 A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     case 7: return launch_one<L3W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+    case W4_256x192:
+    case W4_192x256:
+        // internal: the narrower four-wave tiles, int8 GEMM and linear layer
+        if constexpr ((KIND == KIND_S8 || KIND == KIND_LINEAR) && !CONV) {
+            if (variant == W4_256x192) return launch_w4<KIND, 8, 6>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
+            return launch_w4<KIND, 6, 8>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
+        }
+        return hipErrorInvalidValue;
     case 8:
         return launch_one<std::conditional_t<b1 || KIND == KIND_S4, L4W8, L4W16>, KIND, CONV>(
             A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
@@ -1370,6 +1412,8 @@ int mfma_variant_info(int kind, int variant, int *bm, int *bn, int *bk_bytes, in
     case 6: info_one<L2W16>(bm, bn, bk_bytes, stages); return 0;
     case 7: info_one<L3W8>(bm, bn, bk_bytes, stages); return 0;
     case 8: info_one<L4W16>(bm, bn, bk_bytes, stages); return 0;
+    case W4_256x192: *bm = 256; *bn = 192; *bk_bytes = 128; *stages = 2; return 0;
+    case W4_192x256: *bm = 192; *bn = 256; *bk_bytes = 128; *stages = 2; return 0;
     default: return -1;
     }
 }

@@ -43,8 +43,13 @@
  *   rest with the variant chosen for its own shape.  For the integer GEMMs,
  *   when the chosen variant's tiles fill at most a quarter of the CUs and K is
  *   long, LB_AUTO zeroes C with a kernel and cuts K into bands that add their
- *   exact partial sums into C.  Either way the result is the same (integer
- *   sums do not depend on their order); only the launches differ.  The
+ *   exact partial sums into C.  For the int8 GEMM and the linear layer, when
+ *   the choice is variant 6 and neither applies but its 256x256 tiles would
+ *   fill less than one round of the CUs, LB_AUTO runs the same four-wave
+ *   kernel on 256x192 (or 192x256) tiles if those still fit in one round.
+ *   Either way the result is the same (integer sums do not depend on their
+ *   order; the linear layer's dequantisation is per element); only the
+ *   launches differ (lb_auto_plan reports them).  The
  *   environment variable LB_AUTO_VARIANT, set to one digit 0..8, replaces the
  *   selector's choice for every LB_AUTO call (GEMMs, linear layer and
  *   convolutions) and keeps the splits above: for tuning and tests.  Any other
@@ -189,6 +194,22 @@ int lb_conv2d_s4(const uint8_t *X, const uint8_t *F, int32_t *Y, int64_t N,
  */
 int lb_select_variant(int dtype, int64_t M, int64_t N, int64_t K, int cu_count,
                       int *best, int *second);
+
+/* The launches an LB_AUTO call makes for a shape on the current HIP device,
+ * without launching anything (host-only; for tests and tuning).  op: LB_S8,
+ * LB_S4 or LB_B1 for the GEMMs, LB_PLAN_LINEAR for the int8 linear layer; M, N,
+ * K as for that call.  Writes, through any non-NULL pointer: launches (1, or 2
+ * for the two-launch split), tile_m x tile_n (the workgroup tile of the first
+ * launch: a variant's tile, or 256 x 192 / 192 x 256, the four-wave kernel's
+ * narrower tiles that an automatic choice of variant 6 takes for the int8
+ * GEMM and the linear layer when its 256x256 grid would fill less than one
+ * round of the CUs and the narrower grid still fits in one), and k_bands (K
+ * bands of a single launch; 1: none).  Returns LB_ERR_SHAPE for a
+ * non-positive size (or K below one byte of the type), LB_ERR_VARIANT for an
+ * unknown op. */
+#define LB_PLAN_LINEAR 3
+int lb_auto_plan(int op, int64_t M, int64_t N, int64_t K, int *launches, int *tile_m,
+                 int *tile_n, int *k_bands);
 
 /* Hash of the source files this library was built from (16 hex digits, static
  * storage; never NULL).  The build stamps it in, so that a caller can check a

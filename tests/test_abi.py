@@ -54,6 +54,7 @@ def test_header_constants_match_binding():
     assert define("LB_B1_K_MAX") == lb.K_MAX[lb.LB_B1]
     assert define("LB_CONV_S8_C_ALIGN") == lb.CONV_C_ALIGN[lb.LB_S8]
     assert define("LB_CONV_S4_C_ALIGN") == lb.CONV_C_ALIGN[lb.LB_S4]
+    assert define("LB_PLAN_LINEAR") == lb.LB_PLAN_LINEAR
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
@@ -153,3 +154,19 @@ def test_variant_info(lib):
         lb.lb_variant_info(lb.LB_S8, 9)
     with pytest.raises(lb.LbError):
         lb.lb_variant_info(3, 0)
+
+
+def test_auto_plan_argument_checks(lib):
+    """lb_auto_plan rejects an unknown op and non-positive sizes before it asks
+    the device anything (the launches it reports are checked on the GPU)."""
+    out = [ctypes.c_int(0) for _ in range(4)]
+    refs = [ctypes.byref(v) for v in out]
+    assert lib.lb_auto_plan(4, 64, 64, 64, *refs) == lb.LB_ERR_VARIANT
+    assert lib.lb_auto_plan(-1, 64, 64, 64, *refs) == lb.LB_ERR_VARIANT
+    for op in (lb.LB_S8, lb.LB_S4, lb.LB_B1, lb.LB_PLAN_LINEAR):
+        assert lib.lb_auto_plan(op, 0, 64, 64, *refs) == lb.LB_ERR_SHAPE
+        assert lib.lb_auto_plan(op, 64, -1, 64, *refs) == lb.LB_ERR_SHAPE
+        assert lib.lb_auto_plan(op, 64, 64, 0, *refs) == lb.LB_ERR_SHAPE
+    # K below one byte of a packed type
+    assert lib.lb_auto_plan(lb.LB_S4, 64, 64, 1, *refs) == lb.LB_ERR_SHAPE
+    assert lib.lb_auto_plan(lb.LB_B1, 64, 64, 7, *refs) == lb.LB_ERR_SHAPE

@@ -503,7 +503,7 @@ def test_linear_shard_of_eight_exact(M, N):
     bound."""
     K = 4096
     s = inputs.SEEDS["linear"]
-    print(f"[parity] linear shard {M}x{N}x{K}", flush=True)
+    print(f"[parity] linear shard {M}x{N}x{K}: {lb.lb_auto_plan(lb.LB_PLAN_LINEAR, M, N, K)}", flush=True)
     X, W = inputs.s8_rows(M, K, s[0]), inputs.s8_rows(N, K, s[1])
     sx, sw = inputs.scales(M, s[2]), inputs.scales(N, s[3])
     out = run_linear(X, W, sx, sw, lb.LB_AUTO)
@@ -690,12 +690,70 @@ def test_forced_large_tile_k_bands_match_oracle(forced_auto_variant, kind, v, M,
 
 def test_forced_variant_reaches_the_linear_layer(forced_auto_variant):
     """LB_AUTO_VARIANT also fixes the variant of the linear layer's automatic
-    path (here the four-wave tile on ragged M and N)."""
+    path (here the four-wave kernel, on its 256x192 tile, on ragged M and N)."""
     forced_auto_variant(6)
     M, N, K = 300, 520, 1024
     X, W = inputs.s8_rows(M, K, 81), inputs.s8_rows(N, K, 82)
     sx, sw = inputs.scales(M, 83), inputs.scales(N, 84)
     assert_rel(run_linear(X, W, sx, sw, lb.LB_AUTO), oracle.linear_s8(X, W, sx, sw))
+
+
+# The four-wave kernel's narrower tiles (256x192 and 192x256): an automatic
+# choice of variant 6 takes them for the int8 GEMM and the linear layer when
+# the 256x256 grid would fill less than one round of the CUs and the narrower
+# grid still fits in one.  Ragged edges in both dimensions, K of one alignment
+# unit, a K tail, several stages.
+NARROW = [(512, 380, (256, 192)), (380, 512, (192, 256)), (500, 370, (256, 192)), (370, 500, (192, 256))]
+
+
+def assert_plan(op, M, N, K, launches, tile, bands):
+    plan = lb.lb_auto_plan(op, M, N, K)
+    assert (plan["launches"], (plan["tile_m"], plan["tile_n"]), plan["k_bands"]) == (launches, tile, bands), plan
+
+
+@pytest.mark.parametrize("M,N,tile", NARROW)
+def test_narrow_four_wave_tiles_match_oracle(forced_auto_variant, M, N, tile):
+    forced_auto_variant(6)
+    for K in (16, 64, 1040, 4096):
+        assert_plan(lb.LB_S8, M, N, K, 1, tile, 1)
+        assert_plan(lb.LB_PLAN_LINEAR, M, N, K, 1, tile, 1)
+        print(f"[parity] narrow tile {tile} {M}x{N}x{K}", flush=True)
+        A, B = make("s8", M, N, K, 6100 + K)
+        np.testing.assert_array_equal(run("s8", A, B, lb.LB_AUTO, K), ref("s8", A, B, K))
+        sx, sw = inputs.scales(M, 6200 + K), inputs.scales(N, 6300 + K)
+        assert_rel(run_linear(A, B, sx, sw, lb.LB_AUTO), oracle.linear_s8(A, B, sx, sw))
+
+
+def test_narrow_four_wave_tiles_extreme_values(forced_auto_variant):
+    """All -128 at the largest K through both narrow tiles: every sum is
+    16384 K, 2^31 - 262144 (int8 GEMM), and the linear layer's outputs are that
+    count times sx[m] sw[n]."""
+    forced_auto_variant(6)
+    K = 131056
+    for M, N, tile in ((2304, 2400, (256, 192)), (2400, 2304, (192, 256))):
+        assert_plan(lb.LB_S8, M, N, K, 1, tile, 1)
+        print(f"[parity] narrow tile {tile} extreme {M}x{N}x{K}", flush=True)
+        got = run("s8", np.full((M, K), -128, np.int8), np.full((N, K), -128, np.int8), lb.LB_AUTO)
+        assert (got == 16384 * K).all()
+    M, N = 300, 200
+    assert_plan(lb.LB_PLAN_LINEAR, M, N, K, 1, (192, 256), 1)
+    X = np.full((M, K), -128, np.int8)
+    sx, sw = inputs.scales(M, 6401), inputs.scales(N, 6402)
+    want = 16384.0 * K * np.outer(sx.astype(np.float64), sw.astype(np.float64))
+    assert_rel(run_linear(X, np.full((N, K), -128, np.int8), sx, sw, lb.LB_AUTO), want)
+
+
+@pytest.mark.parametrize("M,N,tile", [(4096, 3072, (256, 192)), (3072, 4096, (192, 256))])
+def test_narrow_four_wave_tiles_full_size(forced_auto_variant, M, N, tile):
+    """One round of narrow tiles filling all 256 CUs (16 x 16 tiles), every
+    element against the oracle."""
+    forced_auto_variant(6)
+    K = 4096
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert_plan(lb.LB_S8, M, N, K, 1, tile, 1)
+    print(f"[parity] narrow tile {tile} {M}x{N}x{K}", flush=True)
+    A, B = make("s8", M, N, K, 6500)
+    np.testing.assert_array_equal(run("s8", A, B, lb.LB_AUTO, K), ref("s8", A, B, K))
 
 
 @pytest.mark.parametrize("kind,M,N,K", [("s8", 64, 64, 8192), ("s8", 4000, 4810, 4096)])
