@@ -756,13 +756,17 @@ def test_narrow_four_wave_tiles_full_size(forced_auto_variant, M, N, tile):
     np.testing.assert_array_equal(run("s8", A, B, lb.LB_AUTO, K), ref("s8", A, B, K))
 
 
-@pytest.mark.parametrize("kind,M,N,K", [("s8", 64, 64, 8192), ("s8", 4000, 4810, 4096)])
+@pytest.mark.parametrize("kind,M,N,K", [("s8", 64, 64, 8192), ("s8", 4000, 4810, 4096), ("s8", 500, 370, 1040)])
 def test_graph_capture_of_automatic_launches(forced_auto_variant, kind, M, N, K):
     """The automatic path's extra launches (the zeroing of C before K bands, or
-    the second launch of a two-launch split) captured into a HIP graph: every
-    replay, with eager work and a clobbered C in between, reproduces the oracle."""
+    the second launch of a two-launch split) and its narrow four-wave tile,
+    captured into a HIP graph: every replay, with eager work and a clobbered C
+    in between, reproduces the oracle."""
     if (M, N) == (64, 64):
         assert k_bands(kind, M, N, K) >= 2
+    elif (M, N) == (500, 370):
+        forced_auto_variant(6)
+        assert_plan(lb.LB_S8, M, N, K, 1, (256, 192), 1)
     else:
         forced_auto_variant(6)
         assert splits(lb.LB_S8, M, N, K, 6)
