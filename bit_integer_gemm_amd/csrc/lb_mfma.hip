@@ -722,7 +722,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t wm = wave >> 1, wn = wave & 1u;
     // A grid 64 tiles wide (or a multiple) takes tiles in row-major order:
     // round robin over the XCDs then gives each XCD every eighth column of
-    // the same rows.  Same-box interleaved timings against the XCD runs with
+    // the same rows.  Same-machine interleaved timings against the XCD runs with
     // bands of 4 rows, int8: 4096 x 16384 x 4096 243.1 against 270.0 us,
     // 16384^2 x 4096 961 against 1058 us; 32 tiles wide it was mixed (8192^2 x
     // 4096 251.4 against 260.8 us, but 2048 x 8192 x 4096 60.8 against 58.3 us
