@@ -696,9 +696,10 @@ __device__ constexpr int spread_item(int s)
 
 // FM x FN: fragment rows and columns of a wave's sub-tile (16 x 16 each); the
 // workgroup tile is (32*FM) x (32*FN).  8 x 8 (256x256) serves every type;
-// 8 x 6 (256x192) and 6 x 8 (192x256) serve the int8 GEMM and the linear layer
-// when a product's 256x256 tiles would fill less than one round of the CUs
-// (the host picks them for an automatic choice).  The copies and the next
+// 8 x 6 (256x192) serves the int8 and int4 GEMMs and the linear layer, 6 x 8
+// (192x256) the int8 GEMM and the linear layer, when a product's 256x256
+// tiles would fill less than one round of the CUs (the host picks them for an
+// automatic choice).  The copies and the next
 // block's fragment reads are spread over a half-block's MFMA slots by
 // spread_item; for 8 x 8 that is the fixed pattern of one copy per four slots
 // and one read per two.
@@ -709,8 +710,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int32_t M, int32_t N, int32_t Kb, uint32_t tiles_m, uint32_t tiles_n, int32_t ldo, int32_t ksplit)
 {
     static_assert(FM % 2 == 0 && FM >= 4 && FM <= 8 && FN % 2 == 0 && FN >= 4 && FN <= 8, "wave sub-tile");
-    static_assert((FM == 8 && FN == 8) || KIND == KIND_S8 || KIND == KIND_LINEAR,
-                  "int4 and 1-bit run the 256x256 tile only");
+    static_assert((FM == 8 && FN == 8) || KIND == KIND_S8 || KIND == KIND_LINEAR ||
+                      (KIND == KIND_S4 && FM == 8 && FN == 6),
+                  "int4 runs the 256x256 and 256x192 tiles, 1-bit the 256x256 tile only");
     constexpr int BM = 32 * FM, BN = 32 * FN;
     constexpr int SS = (BM + BN) * 128;   // one super-stage: 128 K-bytes of A and B
     constexpr int BOFF = BM * 128;        // B's blocks within a super-stage
@@ -1011,8 +1013,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     mfma_tied(acc[i][j], odd ? bhi4[P][j] : blo4[P][j], odd ? ahi : alo);
                     // refill copies: 8-15 in an even block's first half, 0-7 in an
                     // odd block's second half, two per row
+                    // (256x192: the six B copies in rows 0-2 of the even block)
                     const bool cp = second ? P == 1 : (P == 0 && !FIRST);
-                    if (cp && sl % FN == 0) copy_r4((second ? 0 : 8) + (i % (FM / 2)) * 2 + sl / FN);
+                    if constexpr (FN == 8) {
+                        if (cp && sl % FN == 0) copy_r4((second ? 0 : 8) + (i % (FM / 2)) * 2 + sl / FN);
+                    } else {
+                        const int cq = (second ? 0 : 8) + (i % (FM / 2)) * 2 + sl / FN;
+                        if (cp && sl % FN == 0 && cq < FM + FN) copy_r4(cq);
+                    }
                     const int z = (i - FM / 2) * 2 * FN + sl;  // slot in the second half
                     if (second && z < FN) bhi4[Q][z] = *(const i32x4 *)(f + BOFF + (wn * FN + z) * 2048);
                     // the next block's A fragment q replaces fragment q once
@@ -1025,14 +1033,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     // A planes: the next row's even-k plane into alo after this
                     // row's last even-k MFMA (slots 8-13; after row FM-1 the next
                     // block's row 0), this row's odd-k plane into ahi in slots 0-3
-                    // (this row's first odd-k MFMA is at slot 8)
-                    if (sl >= FN && sl < FN + 6) plane_op(sl - FN, fa[(i + 1) % FM], alo, ahi);
+                    // (this row's first odd-k MFMA is at slot 8).  With six
+                    // fragment columns (12 slots a row) the even-k plane takes two
+                    // instructions a slot in slots 6-8, so that it is complete
+                    // three MFMAs before the next row's first.
+                    if constexpr (FN == 8) {
+                        if (sl >= FN && sl < FN + 6) plane_op(sl - FN, fa[(i + 1) % FM], alo, ahi);
+                    } else if (sl >= FN && sl < FN + 3) {
+                        plane_op(2 * (sl - FN), fa[(i + 1) % FM], alo, ahi);
+                        plane_op(2 * (sl - FN) + 1, fa[(i + 1) % FM], alo, ahi);
+                    }
                     if (sl < 4) plane_op(6 + sl, fa[i], alo, ahi);
-                    // the next block's B planes: instruction u at second-half slot 12 + 52u/80
+                    // the next block's B planes: instruction u of 10 FN at
+                    // second-half slot 12 + u (S2 - 12) / (10 FN), S2 the half's
+                    // slots (8 x 8: 12 + 52u/80)
                     if (second && z >= 12) {
+                        constexpr int S2 = FM / 2 * 2 * FN;
 #pragma unroll
                         for (int u = 0; u < 10 * FN; ++u)
-                            if (12 + (u * 52) / (10 * FN) == z)
+                            if (12 + (u * (S2 - 12)) / (10 * FN) == z)
                                 plane_op(u % 10, bhi4[Q][u / 10], blo4[Q][u / 10], bhi4[Q][u / 10]);
                     }
                 }
@@ -1344,9 +1363,17 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     case W4_256x192:
     case W4_192x256:
         // internal: the narrower four-wave tiles, int8 GEMM and linear layer
+        // (both) and int4 GEMM (256x192; under the A/B switch that keeps the
+        // four-wave kernel to int8, int4 takes variant 6's 8-wave tile)
         if constexpr ((KIND == KIND_S8 || KIND == KIND_LINEAR) && !CONV) {
             if (variant == W4_256x192) return launch_w4<KIND, 8, 6>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
             return launch_w4<KIND, 6, 8>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
+        } else if constexpr (KIND == KIND_S4 && !CONV) {
+            if (variant != W4_256x192) return hipErrorInvalidValue;
+            if constexpr (LB_AB_W4_INT8_ONLY)
+                return launch_one<L2W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+            else
+                return launch_w4<KIND, 8, 6>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
         }
         return hipErrorInvalidValue;
     case 8:

@@ -43,10 +43,11 @@
  *   rest with the variant chosen for its own shape.  For the integer GEMMs,
  *   when the chosen variant's tiles fill at most a quarter of the CUs and K is
  *   long, LB_AUTO zeroes C with a kernel and cuts K into bands that add their
- *   exact partial sums into C.  For the int8 GEMM and the linear layer, when
- *   the choice is variant 6 and neither applies but its 256x256 tiles would
- *   fill less than one round of the CUs, LB_AUTO runs the same four-wave
- *   kernel on 256x192 (or 192x256) tiles if those still fit in one round.
+ *   exact partial sums into C.  For the int8 and int4 GEMMs and the linear
+ *   layer, when the choice is variant 6 and neither applies but its 256x256
+ *   tiles would fill less than one round of the CUs, LB_AUTO runs the same
+ *   four-wave kernel on 256x192 tiles (int8 and linear: or 192x256) if those
+ *   still fit in one round.
  *   Either way the result is the same (integer sums do not depend on their
  *   order; the linear layer's dequantisation is per element); only the
  *   launches differ (lb_auto_plan reports them).  The
@@ -202,8 +203,8 @@ int lb_select_variant(int dtype, int64_t M, int64_t N, int64_t K, int cu_count,
  * for the two-launch split), tile_m x tile_n (the workgroup tile of the first
  * launch: a variant's tile, or 256 x 192 / 192 x 256, the four-wave kernel's
  * narrower tiles that an automatic choice of variant 6 takes for the int8
- * GEMM and the linear layer when its 256x256 grid would fill less than one
- * round of the CUs and the narrower grid still fits in one), and k_bands (K
+ * and int4 GEMMs and the linear layer when its 256x256 grid would fill less
+ * than one round of the CUs and the narrower grid still fits in one), and k_bands (K
  * bands of a single launch; 1: none).  Returns LB_ERR_SHAPE for a
  * non-positive size (or K below one byte of the type), LB_ERR_VARIANT for an
  * unknown op. */

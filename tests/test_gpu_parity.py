@@ -724,6 +724,18 @@ def test_narrow_four_wave_tiles_match_oracle(forced_auto_variant, M, N, tile):
         assert_rel(run_linear(A, B, sx, sw, lb.LB_AUTO), oracle.linear_s8(A, B, sx, sw))
 
 
+@pytest.mark.parametrize("M,N", [(512, 380), (380, 512), (500, 370), (370, 500)])
+def test_narrow_four_wave_tile_int4_matches_oracle(forced_auto_variant, M, N):
+    """int4 takes the 256x192 narrow tile in either orientation (its unpack
+    schedule exists for six fragment columns, not six rows)."""
+    forced_auto_variant(6)
+    for K in (32, 64, 1056, 4096):
+        assert_plan(lb.LB_S4, M, N, K, 1, (256, 192), 1)
+        print(f"[parity] narrow tile int4 {M}x{N}x{K}", flush=True)
+        A, B = make("s4", M, N, K, 6600 + K)
+        np.testing.assert_array_equal(run("s4", A, B, lb.LB_AUTO, K), ref("s4", A, B, K))
+
+
 def test_narrow_four_wave_tiles_extreme_values(forced_auto_variant):
     """All -128 at the largest K through both narrow tiles: every sum is
     16384 K, 2^31 - 262144 (int8 GEMM), and the linear layer's outputs are that
@@ -735,6 +747,12 @@ def test_narrow_four_wave_tiles_extreme_values(forced_auto_variant):
         print(f"[parity] narrow tile {tile} extreme {M}x{N}x{K}", flush=True)
         got = run("s8", np.full((M, K), -128, np.int8), np.full((N, K), -128, np.int8), lb.LB_AUTO)
         assert (got == 16384 * K).all()
+    M, N, K4 = 2304, 2400, 131040
+    assert_plan(lb.LB_S4, M, N, K4, 1, (256, 192), 1)
+    print(f"[parity] narrow tile int4 extreme {M}x{N}x{K4}", flush=True)
+    A4 = inputs.pack_s4(np.full((M, K4), -8, np.int8))
+    got = run("s4", A4, inputs.pack_s4(np.full((N, K4), -8, np.int8)), lb.LB_AUTO)
+    assert (got == 64 * K4).all()
     M, N = 300, 200
     assert_plan(lb.LB_PLAN_LINEAR, M, N, K, 1, (192, 256), 1)
     X = np.full((M, K), -128, np.int8)
@@ -743,17 +761,18 @@ def test_narrow_four_wave_tiles_extreme_values(forced_auto_variant):
     assert_rel(run_linear(X, np.full((N, K), -128, np.int8), sx, sw, lb.LB_AUTO), want)
 
 
-@pytest.mark.parametrize("M,N,tile", [(4096, 3072, (256, 192)), (3072, 4096, (192, 256))])
-def test_narrow_four_wave_tiles_full_size(forced_auto_variant, M, N, tile):
+@pytest.mark.parametrize("kind,M,N,tile", [("s8", 4096, 3072, (256, 192)), ("s8", 3072, 4096, (192, 256)),
+                                            ("s4", 4096, 3072, (256, 192))])
+def test_narrow_four_wave_tiles_full_size(forced_auto_variant, kind, M, N, tile):
     """One round of narrow tiles filling all 256 CUs (16 x 16 tiles), every
     element against the oracle."""
     forced_auto_variant(6)
     K = 4096
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert_plan(lb.LB_S8, M, N, K, 1, tile, 1)
-    print(f"[parity] narrow tile {tile} {M}x{N}x{K}", flush=True)
-    A, B = make("s8", M, N, K, 6500)
-    np.testing.assert_array_equal(run("s8", A, B, lb.LB_AUTO, K), ref("s8", A, B, K))
+        assert_plan(lb.LB_S8 if kind == "s8" else lb.LB_S4, M, N, K, 1, tile, 1)
+    print(f"[parity] narrow tile {kind} {tile} {M}x{N}x{K}", flush=True)
+    A, B = make(kind, M, N, K, 6500)
+    np.testing.assert_array_equal(run(kind, A, B, lb.LB_AUTO, K), ref(kind, A, B, K))
 
 
 @pytest.mark.parametrize("kind,M,N,K", [("s8", 64, 64, 8192), ("s8", 4000, 4810, 4096), ("s8", 500, 370, 1040)])
