@@ -736,6 +736,46 @@ def test_narrow_four_wave_tile_int4_matches_oracle(forced_auto_variant, M, N):
         np.testing.assert_array_equal(run("s4", A, B, lb.LB_AUTO, K), ref("s4", A, B, K))
 
 
+def _narrow_random_cases(n=12, seed=6700):
+    """Seeded partial-round shapes: M, N in 600..4000 (ragged), K a random
+    multiple of 32 up to 3200; each case names its op and the narrow tile it
+    must take on a 256-CU GPU."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        M, N = (int(v) for v in rng.integers(600, 4001, 2))
+        K = 32 * int(rng.integers(1, 101))
+        t256 = -(-M // 256) * -(-N // 256)
+        wide, tall = -(-M // 256) * -(-N // 192), -(-M // 192) * -(-N // 256)
+        if t256 >= 256 or 4 * t256 <= 256:      # a partial round, not few enough tiles for K bands
+            continue
+        op = ("s8", "s4", "linear")[len(cases) % 3]
+        if wide <= 256 and (op == "s4" or tall > 256 or wide <= tall):
+            tile = (256, 192)
+        elif tall <= 256 and op != "s4":
+            tile = (192, 256)
+        else:
+            continue
+        cases.append((op, M, N, K, tile))
+    return cases
+
+
+@pytest.mark.parametrize("op,M,N,K,tile", _narrow_random_cases())
+def test_narrow_four_wave_tiles_random_shapes(forced_auto_variant, op, M, N, K, tile):
+    forced_auto_variant(6)
+    code = {"s8": lb.LB_S8, "s4": lb.LB_S4, "linear": lb.LB_PLAN_LINEAR}[op]
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert_plan(code, M, N, K, 1, tile, 1)
+    print(f"[parity] narrow random {op} {M}x{N}x{K} {tile}", flush=True)
+    if op == "linear":
+        X, W = inputs.s8_rows(M, K, 6800 + K), inputs.s8_rows(N, K, 6801 + K)
+        sx, sw = inputs.scales(M, 6802), inputs.scales(N, 6803)
+        assert_rel(run_linear(X, W, sx, sw, lb.LB_AUTO), oracle.linear_s8(X, W, sx, sw))
+    else:
+        A, B = make(op, M, N, K, 6900 + K)
+        np.testing.assert_array_equal(run(op, A, B, lb.LB_AUTO, K), ref(op, A, B, K))
+
+
 def test_narrow_four_wave_tiles_extreme_values(forced_auto_variant):
     """All -128 at the largest K through both narrow tiles: every sum is
     16384 K, 2^31 - 262144 (int8 GEMM), and the linear layer's outputs are that
