@@ -99,15 +99,16 @@ int plan_parts(int dtype, int variant, int64_t M, int64_t N, int64_t K, Part *pa
 // int8 GEMM or the linear layer is the four-wave 256x256 tile (variant 6) and
 // its grid has fewer tiles than the chip has CUs, the product runs on 256x192
 // tiles instead (else 192x256, whichever grid is smaller) if that grid still
-// fits in one round: every CU then does a quarter less work.  The int4 GEMM
-// takes the 256x192 tile the same way (its unpack schedule exists for eight
-// and six fragment columns, not for six rows).  Measured on
+// fits in one round: every CU then does a quarter less work.  The int4 and
+// 1-bit (FP4 route) GEMMs take the 256x192 tile the same way (their plane
+// schedules exist for eight and six fragment columns, not for six rows).
+// Measured on
 // MI355X, identical results: 8192 x 1376 x 4096 (linear) 47.5 against 53.6
 // us, 1024 x 11008 x 4096 (linear) 46.3 against 54.0 us, int8 4096 x 3072 x
 // 4096 48.4 against 54.2 us, 3072 x 4096 x 4096 (192x256) 48.2 against 53.3 us.
 int narrow_w4_tile(int kind, int variant, int64_t M, int64_t N)
 {
-    const bool s4 = kind == lb::KIND_S4;
+    const bool s4 = kind == lb::KIND_S4 || kind == lb::KIND_B1F4;   // 256x192 only
     if (variant != 6 || (kind != lb::KIND_S8 && kind != lb::KIND_LINEAR && !s4)) return variant;
     int cu = 0;
     if (lb::device_cu_count(&cu) != LB_OK || cu <= 0) return variant;

@@ -12,8 +12,8 @@ namespace lb {
 enum { KIND_S8 = 0, KIND_S4 = 1, KIND_LINEAR = 2, KIND_B1 = 3, KIND_B1F4 = 4 };
 
 // Internal tile codes beside the nine public variants (never accepted from a
-// caller): the four-wave kernel on 256x192 tiles (int8 and int4 GEMMs, linear
-// layer) and on 192x256 tiles (int8 GEMM, linear layer).
+// caller): the four-wave kernel on 256x192 tiles (int8, int4 and 1-bit FP4-
+// route GEMMs, linear layer) and on 192x256 tiles (int8 GEMM, linear layer).
 enum { W4_256x192 = 16, W4_192x256 = 17 };
 
 // int8 MFMA family (int8 GEMM, packed-int4 GEMM, int8 linear layer, and the

@@ -696,8 +696,8 @@ __device__ constexpr int spread_item(int s)
 
 // FM x FN: fragment rows and columns of a wave's sub-tile (16 x 16 each); the
 // workgroup tile is (32*FM) x (32*FN).  8 x 8 (256x256) serves every type;
-// 8 x 6 (256x192) serves the int8 and int4 GEMMs and the linear layer, 6 x 8
-// (192x256) the int8 GEMM and the linear layer, when a product's 256x256
+// 8 x 6 (256x192) serves every type, 6 x 8 (192x256) the int8 GEMM and the
+// linear layer, when a product's 256x256
 // tiles would fill less than one round of the CUs (the host picks them for an
 // automatic choice).  The copies and the next
 // block's fragment reads are spread over a half-block's MFMA slots by
@@ -711,8 +711,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 {
     static_assert(FM % 2 == 0 && FM >= 4 && FM <= 8 && FN % 2 == 0 && FN >= 4 && FN <= 8, "wave sub-tile");
     static_assert((FM == 8 && FN == 8) || KIND == KIND_S8 || KIND == KIND_LINEAR ||
-                      (KIND == KIND_S4 && FM == 8 && FN == 6),
-                  "int4 runs the 256x256 and 256x192 tiles, 1-bit the 256x256 tile only");
+                      ((KIND == KIND_S4 || KIND == KIND_B1F4) && FM == 8 && FN == 6),
+                  "int4 and 1-bit run the 256x256 and 256x192 tiles");
     constexpr int BM = 32 * FM, BN = 32 * FN;
     constexpr int SS = (BM + BN) * 128;   // one super-stage: 128 K-bytes of A and B
     constexpr int BOFF = BM * 128;        // B's blocks within a super-stage
@@ -1159,21 +1159,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     // refill copies: 8-15 in an even block's first half, 0-7 in an
                     // odd block's second half, one per 16 MFMAs
                     const bool cp = H == 1 ? P == 1 : (P == 0 && !FIRST);
-                    if (cp && j == 0 && r % 2 == 0) copy_r4((H == 1 ? 0 : 8) + (r % (2 * FM)) / 2);
-                    if (p == 3) {
-                        // plane 3: the next block's fragments
-                        if (i == 0) fb[j] = *(const i32x4 *)(f + BOFF + (wn * FN + j) * 2048);
-                        if (j == 6) fa[i] = *(const i32x4 *)(f + (wm * FM + i) * 2048);
-                    }
-                    // A plane of the next row: slots 1 ..
-                    if (j >= 1 && j - 1 < nops(pn)) plane_op(pn, j - 1, fa[in], ap[(r + 1) % 2]);
-                    // B plane p+1 of fragment i (plane 3: the next block's plane 0
-                    // of fragment i-1, and of fragment 7 too in row (3, 7))
-                    if (p < 3) {
-                        if (j >= 2 && j - 2 < nops(p + 1)) plane_op(p + 1, j - 2, fb[i], bp[(p + 1) % 2][i]);
-                    } else if (i >= 1) {
-                        if (j >= 2 && j < 6) plane_op(0, j - 2, fb[i - 1], bp[0][i - 1]);
-                        if (i == FM - 1 && j >= 4) plane_op(0, j - 4, fb[FM - 1], bp[0][FM - 1]);
+                    if constexpr (FN != 8) {
+                        // Six fragment columns (six MFMA slots a row): the six B
+                        // copies go out in the first six even rows; the next
+                        // row's A plane takes slots 0-3 (done two MFMAs before
+                        // that row); B plane p+1 of the six fragments spreads
+                        // over the plane's slots 2-45; the next block's A
+                        // fragment i is read at the last slot of row (3, i).
+                        const int cq = (H == 1 ? 0 : 8) + (r % (2 * FM)) / 2;
+                        if (cp && j == 0 && r % 2 == 0 && cq < FM + FN) copy_r4(cq);
+                        if (p == 3) {
+                            if (i == 0) fb[j] = *(const i32x4 *)(f + BOFF + (wn * FN + j) * 2048);
+                            if (j == FN - 1) fa[i] = *(const i32x4 *)(f + (wm * FM + i) * 2048);
+                        }
+#pragma unroll
+                        for (int k = 0; k < 6; ++k)
+                            if (k < nops(pn) && k * 4 / nops(pn) == j) plane_op(pn, k, fa[in], ap[(r + 1) % 2]);
+                        if (p < 3) {
+                            const int g = i * FN + j, nk = nops(p + 1), nb = FN * nk;
+#pragma unroll
+                            for (int u = 0; u < FN * 6; ++u)
+                                if (u < nb && 2 + u * 43 / nb == g)
+                                    plane_op(p + 1, u % nk, fb[u / nk], bp[(p + 1) % 2][u / nk]);
+                        } else if (i >= 1 && i - 1 < FN) {
+                            if (j >= 2 && j < 6) plane_op(0, j - 2, fb[i - 1], bp[0][i - 1]);
+                        }
+                    } else {
+                        if (cp && j == 0 && r % 2 == 0) copy_r4((H == 1 ? 0 : 8) + (r % (2 * FM)) / 2);
+                        if (p == 3) {
+                            // plane 3: the next block's fragments
+                            if (i == 0) fb[j] = *(const i32x4 *)(f + BOFF + (wn * FN + j) * 2048);
+                            if (j == 6) fa[i] = *(const i32x4 *)(f + (wm * FM + i) * 2048);
+                        }
+                        // A plane of the next row: slots 1 ..
+                        if (j >= 1 && j - 1 < nops(pn)) plane_op(pn, j - 1, fa[in], ap[(r + 1) % 2]);
+                        // B plane p+1 of fragment i (plane 3: the next block's plane 0
+                        // of fragment i-1, and of fragment 7 too in row (3, 7))
+                        if (p < 3) {
+                            if (j >= 2 && j - 2 < nops(p + 1)) plane_op(p + 1, j - 2, fb[i], bp[(p + 1) % 2][i]);
+                        } else if (i >= 1) {
+                            if (j >= 2 && j < 6) plane_op(0, j - 2, fb[i - 1], bp[0][i - 1]);
+                            if (i == FM - 1 && j >= 4) plane_op(0, j - 4, fb[FM - 1], bp[0][FM - 1]);
+                        }
                     }
                 }
             }
@@ -1363,12 +1390,13 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
     case W4_256x192:
     case W4_192x256:
         // internal: the narrower four-wave tiles, int8 GEMM and linear layer
-        // (both) and int4 GEMM (256x192; under the A/B switch that keeps the
-        // four-wave kernel to int8, int4 takes variant 6's 8-wave tile)
+        // (both), int4 and 1-bit FP4-route GEMMs (256x192; under the A/B switch
+        // that keeps the four-wave kernel to int8 they take variant 6's
+        // 8-wave tile)
         if constexpr ((KIND == KIND_S8 || KIND == KIND_LINEAR) && !CONV) {
             if (variant == W4_256x192) return launch_w4<KIND, 8, 6>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
             return launch_w4<KIND, 6, 8>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, s);
-        } else if constexpr (KIND == KIND_S4 && !CONV) {
+        } else if constexpr ((KIND == KIND_S4 || KIND == KIND_B1F4) && !CONV) {
             if (variant != W4_256x192) return hipErrorInvalidValue;
             if constexpr (LB_AB_W4_INT8_ONLY)
                 return launch_one<L2W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);

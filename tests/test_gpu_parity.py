@@ -736,10 +736,10 @@ def test_narrow_four_wave_tile_int4_matches_oracle(forced_auto_variant, M, N):
         np.testing.assert_array_equal(run("s4", A, B, lb.LB_AUTO, K), ref("s4", A, B, K))
 
 
-def _narrow_random_cases(n=12, seed=6700):
+def _narrow_random_cases(n=16, seed=6700):
     """Seeded partial-round shapes: M, N in 600..4000 (ragged), K a random
-    multiple of 32 up to 3200; each case names its op and the narrow tile it
-    must take on a 256-CU GPU."""
+    multiple of 32 up to 3200 (1-bit: of 128 up to 12800); each case names its
+    op and the narrow tile it must take on a 256-CU GPU."""
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
@@ -749,10 +749,12 @@ def _narrow_random_cases(n=12, seed=6700):
         wide, tall = -(-M // 256) * -(-N // 192), -(-M // 192) * -(-N // 256)
         if t256 >= 256 or 4 * t256 <= 256:      # a partial round, not few enough tiles for K bands
             continue
-        op = ("s8", "s4", "linear")[len(cases) % 3]
-        if wide <= 256 and (op == "s4" or tall > 256 or wide <= tall):
+        op = ("s8", "s4", "linear", "b1")[len(cases) % 4]
+        if op == "b1":
+            K *= 4
+        if wide <= 256 and (op in ("s4", "b1") or tall > 256 or wide <= tall):
             tile = (256, 192)
-        elif tall <= 256 and op != "s4":
+        elif tall <= 256 and op in ("s8", "linear"):
             tile = (192, 256)
         else:
             continue
@@ -763,7 +765,7 @@ def _narrow_random_cases(n=12, seed=6700):
 @pytest.mark.parametrize("op,M,N,K,tile", _narrow_random_cases())
 def test_narrow_four_wave_tiles_random_shapes(forced_auto_variant, op, M, N, K, tile):
     forced_auto_variant(6)
-    code = {"s8": lb.LB_S8, "s4": lb.LB_S4, "linear": lb.LB_PLAN_LINEAR}[op]
+    code = {"s8": lb.LB_S8, "s4": lb.LB_S4, "b1": lb.LB_B1, "linear": lb.LB_PLAN_LINEAR}[op]
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
         assert_plan(code, M, N, K, 1, tile, 1)
     print(f"[parity] narrow random {op} {M}x{N}x{K} {tile}", flush=True)
@@ -774,6 +776,32 @@ def test_narrow_four_wave_tiles_random_shapes(forced_auto_variant, op, M, N, K, 
     else:
         A, B = make(op, M, N, K, 6900 + K)
         np.testing.assert_array_equal(run(op, A, B, lb.LB_AUTO, K), ref(op, A, B, K))
+
+
+@pytest.mark.parametrize("M,N", [(512, 380), (380, 512), (500, 370)])
+def test_narrow_four_wave_tile_b1_matches_oracle(forced_auto_variant, M, N):
+    """The 1-bit GEMM (FP4 route) takes the 256x192 narrow tile in either
+    orientation (its plane schedule exists for six fragment columns)."""
+    forced_auto_variant(6)
+    for K in (128, 1024, 8320, 16384):
+        assert_plan(lb.LB_B1, M, N, K, 1, (256, 192), 1)
+        print(f"[parity] narrow tile 1-bit {M}x{N}x{K}", flush=True)
+        A, B = make("b1", M, N, K, 6650 + K)
+        np.testing.assert_array_equal(run("b1", A, B, lb.LB_AUTO, K), ref("b1", A, B, K))
+
+
+def test_narrow_four_wave_tile_b1_extreme_values(forced_auto_variant):
+    """All ones at 2^20 bits through the 1-bit narrow tile give K; 0x55.. against
+    0xAA.. gives 0."""
+    forced_auto_variant(6)
+    M, N, K = 2304, 2400, 1 << 20
+    assert_plan(lb.LB_B1, M, N, K, 1, (256, 192), 1)
+    print(f"[parity] narrow tile 1-bit extreme {M}x{N}x{K}", flush=True)
+    ones = np.full((M, K // 32), 0xFFFFFFFF, np.uint32)
+    assert (run("b1", ones, ones[:N], lb.LB_AUTO) == K).all()
+    fives = np.full((M, K // 32), 0x55555555, np.uint32)
+    aas = np.full((N, K // 32), 0xAAAAAAAA, np.uint32)
+    assert (run("b1", fives, aas, lb.LB_AUTO) == 0).all()
 
 
 def test_narrow_four_wave_tiles_extreme_values(forced_auto_variant):
@@ -802,14 +830,14 @@ def test_narrow_four_wave_tiles_extreme_values(forced_auto_variant):
 
 
 @pytest.mark.parametrize("kind,M,N,tile", [("s8", 4096, 3072, (256, 192)), ("s8", 3072, 4096, (192, 256)),
-                                            ("s4", 4096, 3072, (256, 192))])
+                                            ("s4", 4096, 3072, (256, 192)), ("b1", 4096, 3072, (256, 192))])
 def test_narrow_four_wave_tiles_full_size(forced_auto_variant, kind, M, N, tile):
     """One round of narrow tiles filling all 256 CUs (16 x 16 tiles), every
     element against the oracle."""
     forced_auto_variant(6)
-    K = 4096
+    K = 8192 if kind == "b1" else 4096
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert_plan(lb.LB_S8 if kind == "s8" else lb.LB_S4, M, N, K, 1, tile, 1)
+        assert_plan({"s8": lb.LB_S8, "s4": lb.LB_S4, "b1": lb.LB_B1}[kind], M, N, K, 1, tile, 1)
     print(f"[parity] narrow tile {kind} {tile} {M}x{N}x{K}", flush=True)
     A, B = make(kind, M, N, K, 6500)
     np.testing.assert_array_equal(run(kind, A, B, lb.LB_AUTO, K), ref(kind, A, B, K))

@@ -192,9 +192,8 @@ def kernels(tmp_path_factory):
 def test_every_kernel_was_disassembled(kernels):
     names = [f.name for f in kernels]
     w4 = [n for n in names if "mfma_w4_kernel" in n]
-    # 256x256: int8, int4, linear, 1-bit (FP4); 256x192: int8, int4, linear;
-    # 192x256: int8, linear
-    assert len(w4) == 9, w4
+    # 256x256 and 256x192: int8, int4, linear, 1-bit (FP4); 192x256: int8, linear
+    assert len(w4) == 10, w4
     assert sum("mfma_gemm_kernel" in n for n in names) >= 9
     for f in kernels:
         if "mfma_w4_kernel" in f.name:
