@@ -106,17 +106,45 @@ int plan_parts(int dtype, int variant, int64_t M, int64_t N, int64_t K, Part *pa
 // MI355X, identical results: 8192 x 1376 x 4096 (linear) 47.5 against 53.6
 // us, 1024 x 11008 x 4096 (linear) 46.3 against 54.0 us, int8 4096 x 3072 x
 // 4096 48.4 against 54.2 us, 3072 x 4096 x 4096 (192x256) 48.2 against 53.3 us.
-int narrow_w4_tile(int kind, int variant, int64_t M, int64_t N)
+// The narrow tile (W4_256x192 or W4_192x256) a product of this kind would take
+// on one partial round, and its tile count; 0 if none applies.
+int narrow_tile_of(int kind, int64_t M, int64_t N, int64_t *count)
 {
     const bool s4 = kind == lb::KIND_S4 || kind == lb::KIND_B1F4;   // 256x192 only
-    if (variant != 6 || (kind != lb::KIND_S8 && kind != lb::KIND_LINEAR && !s4)) return variant;
+    if (kind != lb::KIND_S8 && kind != lb::KIND_LINEAR && !s4) return 0;
+    int cu = 0;
+    if (lb::device_cu_count(&cu) != LB_OK || cu <= 0) return 0;
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (tiles(256, 256) >= cu) return 0;
+    const int64_t wide = tiles(256, 192), tall = tiles(192, 256);
+    if (wide <= cu && (s4 || tall > cu || wide <= tall)) { *count = wide; return lb::W4_256x192; }
+    if (tall <= cu && !s4) { *count = tall; return lb::W4_192x256; }
+    return 0;
+}
+
+int narrow_w4_tile(int kind, int variant, int64_t M, int64_t N)
+{
+    int64_t count = 0;
+    const int t = variant == 6 ? narrow_tile_of(kind, M, N, &count) : 0;
+    return t ? t : variant;
+}
+
+// A nearly full round of narrow tiles beats the selector's choice.  The
+// selection table and network know the nine variants only.  Measured on MI355X
+// over partial-round shapes (M x N from 1536 x 8192 to 5120 x 2304, int4 K 2048-
+// 8192, 1-bit K 8192-32768 bits): where the narrow grid had at least 7/8 as many
+// tiles as CUs, variant 6 on it was 1.12-1.16x faster (int4) and 1.11-1.22x
+// (1-bit) than the medium tile the selector chose, on every shape; with 176 or
+// fewer tiles the selector's choice was faster (1.01-1.32x).  The int8 selector
+// already chose variant 6 on every shape above that fill.  An automatic choice
+// (not one fixed by LB_AUTO_VARIANT) is therefore replaced by variant 6 there.
+int prefer_full_narrow_round(int kind, int variant, int64_t M, int64_t N)
+{
+    if (variant == 6 || auto_override() >= 0) return variant;
     int cu = 0;
     if (lb::device_cu_count(&cu) != LB_OK || cu <= 0) return variant;
-    auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 256) >= cu) return variant;
-    const int64_t wide = tiles(256, 192), tall = tiles(192, 256);
-    if (wide <= cu && (s4 || tall > cu || wide <= tall)) return lb::W4_256x192;
-    if (tall <= cu && !s4) return lb::W4_192x256;
+    int64_t count = 0;
+    if (narrow_tile_of(kind, M, N, &count) && 8 * count >= 7 * (int64_t)cu) return 6;
     return variant;
 }
 
@@ -226,7 +254,7 @@ Plan make_plan(int kind, int dtype, int variant, int64_t M, int64_t N, int64_t K
         p.zero = true;
         p.parts[0].variant = variant;
     } else if (variant == LB_AUTO) {
-        const int v = resolve(dtype, LB_AUTO, M, N, K);
+        const int v = prefer_full_narrow_round(kind, resolve(dtype, LB_AUTO, M, N, K), M, N);
         p.np = plan_parts(dtype, v, M, N, K, p.parts);
         if (p.np == 1 && plan_ksplit(kind, v, M, N, kb, &p.band) > 1)
             p.zero = true;

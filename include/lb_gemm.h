@@ -47,7 +47,9 @@
  *   layer, when the choice is variant 6 and neither applies but its 256x256
  *   tiles would fill less than one round of the CUs, LB_AUTO runs the same
  *   four-wave kernel on 256x192 tiles (int8 and linear: or 192x256) if those
- *   still fit in one round.
+ *   still fit in one round; and where such a round of narrower tiles would
+ *   fill at least 7/8 of the CUs, LB_AUTO takes variant 6 for it whatever the
+ *   selector chose (not when LB_AUTO_VARIANT fixes the variant).
  *   Either way the result is the same (integer sums do not depend on their
  *   order; the linear layer's dequantisation is per element); only the
  *   launches differ (lb_auto_plan reports them).  The

@@ -804,6 +804,29 @@ def test_narrow_four_wave_tile_b1_extreme_values(forced_auto_variant):
     assert (run("b1", fives, aas, lb.LB_AUTO) == 0).all()
 
 
+@pytest.mark.parametrize("kind,M,N,K,narrow", [
+    ("s4", 4096, 3072, 2048, True), ("s4", 5120, 2304, 2048, True), ("b1", 8192, 1536, 8192, True),
+    ("b1", 2816, 4096, 16384, True), ("s4", 2048, 4096, 2048, False), ("b1", 2304, 2400, 8192, False),
+])
+def test_automatic_choice_takes_a_nearly_full_narrow_round(kind, M, N, K, narrow):
+    """Without LB_AUTO_VARIANT: where a round of 256x192 tiles fills at least
+    7/8 of the CUs the automatic path runs it (variant 6), whatever the
+    selector chose; with fewer narrow tiles it keeps the selector's tile.  The
+    result matches the oracle either way."""
+    assert "LB_AUTO_VARIANT" not in os.environ
+    code = {"s4": lb.LB_S4, "b1": lb.LB_B1}[kind]
+    plan = lb.lb_auto_plan(code, M, N, K)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        if narrow:
+            assert (plan["tile_m"], plan["tile_n"], plan["launches"]) == (256, 192, 1), plan
+        else:
+            info = lb.lb_variant_info(code, lb.lb_select_variant(code, M, N, K, 0)[0])
+            assert (plan["tile_m"], plan["tile_n"]) == (info["tile_m"], info["tile_n"]), plan
+    print(f"[parity] automatic narrow round {kind} {M}x{N}x{K}: {plan}", flush=True)
+    A, B = make(kind, M, N, K, 7100)
+    np.testing.assert_array_equal(run(kind, A, B, lb.LB_AUTO, K), ref(kind, A, B, K))
+
+
 def test_narrow_four_wave_tiles_extreme_values(forced_auto_variant):
     """All -128 at the largest K through both narrow tiles: every sum is
     16384 K, 2^31 - 262144 (int8 GEMM), and the linear layer's outputs are that
