@@ -88,7 +88,7 @@ def load(path: str = LIB_PATH):
     lib.lb_status_string.restype = ctypes.c_char_p
     lib.lb_variant_info.argtypes = [i32, i32, ip, ip, ip, ip]
     lib.lb_variant_info.restype = i32
-    lib.lb_auto_plan.argtypes = [i32, i64, i64, i64, ip, ip, ip, ip]
+    lib.lb_auto_plan.argtypes = [i32, i64, i64, i64, i32, ip, ip, ip, ip]
     lib.lb_auto_plan.restype = i32
     _lib = lib
     return lib
@@ -248,12 +248,12 @@ def lb_variant_info(dtype: int, variant: int) -> dict:
     return dict(zip(("tile_m", "tile_n", "tile_k", "stages"), (v.value for v in vals)))
 
 
-def lb_auto_plan(op: int, M: int, N: int, K: int) -> dict:
-    """What an LB_AUTO call makes for a shape on the current device: the number
-    of launches, the first launch's workgroup tile and its K bands.  op: LB_S8,
-    LB_S4, LB_B1 or LB_PLAN_LINEAR."""
+def lb_auto_plan(op: int, M: int, N: int, K: int, cu_count: int = 0) -> dict:
+    """What an LB_AUTO call makes for a shape: the number of launches, the first
+    launch's workgroup tile and its K bands.  op: LB_S8, LB_S4, LB_B1 or
+    LB_PLAN_LINEAR; cu_count <= 0 plans for the current device."""
     vals = [ctypes.c_int(0) for _ in range(4)]
-    _raise(load().lb_auto_plan(op, M, N, K, *[ctypes.byref(v) for v in vals]), "lb_auto_plan")
+    _raise(load().lb_auto_plan(op, M, N, K, cu_count, *[ctypes.byref(v) for v in vals]), "lb_auto_plan")
     return dict(zip(("launches", "tile_m", "tile_n", "k_bands"), (v.value for v in vals)))
 
 

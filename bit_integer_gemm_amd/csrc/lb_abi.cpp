@@ -41,14 +41,14 @@ int auto_override()
     return e[0] - '0';
 }
 
-int resolve(int dtype, int variant, int64_t M, int64_t N, int64_t K)
+int resolve(int dtype, int variant, int64_t M, int64_t N, int64_t K, int cu)
 {
     if (variant != LB_AUTO) return variant;
     const int forced = auto_override();
     if (forced >= 0) return forced;
     int best = LB_DEFAULT_VARIANT;
     // cu_count 0: ask the current device; any failure keeps the default.
-    if (lb::select_from_table(dtype, M, N, K, 0, &best, nullptr) != LB_OK) return LB_DEFAULT_VARIANT;
+    if (lb::select_from_table(dtype, M, N, K, cu, &best, nullptr) != LB_OK) return LB_DEFAULT_VARIANT;
     return best;
 }
 
@@ -67,12 +67,10 @@ struct Part {
     int variant;
 };
 
-int plan_parts(int dtype, int variant, int64_t M, int64_t N, int64_t K, Part *parts)
+int plan_parts(int dtype, int variant, int64_t M, int64_t N, int64_t K, int cu, Part *parts)
 {
     parts[0] = {0, M, 0, N, variant};
-    if (variant < 6) return 1;
-    int cu = 0;
-    if (lb::device_cu_count(&cu) != LB_OK || cu <= 0) return 1;
+    if (variant < 6 || cu <= 0) return 1;
     const int64_t tile = 256;
     const int64_t tm = (M + tile - 1) / tile, tn = (N + tile - 1) / tile, T = tm * tn;
     if (T <= cu || T % cu == 0 || 2 * (T % cu) > cu) return 1;
@@ -81,7 +79,7 @@ int plan_parts(int dtype, int variant, int64_t M, int64_t N, int64_t K, Part *pa
     if (c > 0) {
         const int64_t n1 = c * tile;
         parts[0] = {0, M, 0, n1, variant};
-        parts[1] = {0, M, n1, N - n1, resolve(dtype, LB_AUTO, M, N - n1, K)};
+        parts[1] = {0, M, n1, N - n1, resolve(dtype, LB_AUTO, M, N - n1, K, cu)};
         return 2;
     }
     int64_t r = tm - 1;
@@ -89,7 +87,7 @@ int plan_parts(int dtype, int variant, int64_t M, int64_t N, int64_t K, Part *pa
     if (r > 0) {
         const int64_t m1 = r * tile;
         parts[0] = {0, m1, 0, N, variant};
-        parts[1] = {m1, M - m1, 0, N, resolve(dtype, LB_AUTO, M - m1, N, K)};
+        parts[1] = {m1, M - m1, 0, N, resolve(dtype, LB_AUTO, M - m1, N, K, cu)};
         return 2;
     }
     return 1;
@@ -108,12 +106,10 @@ int plan_parts(int dtype, int variant, int64_t M, int64_t N, int64_t K, Part *pa
 // 4096 48.4 against 54.2 us, 3072 x 4096 x 4096 (192x256) 48.2 against 53.3 us.
 // The narrow tile (W4_256x192 or W4_192x256) a product of this kind would take
 // on one partial round, and its tile count; 0 if none applies.
-int narrow_tile_of(int kind, int64_t M, int64_t N, int64_t *count)
+int narrow_tile_of(int kind, int64_t M, int64_t N, int cu, int64_t *count)
 {
     const bool s4 = kind == lb::KIND_S4 || kind == lb::KIND_B1F4;   // 256x192 only
-    if (kind != lb::KIND_S8 && kind != lb::KIND_LINEAR && !s4) return 0;
-    int cu = 0;
-    if (lb::device_cu_count(&cu) != LB_OK || cu <= 0) return 0;
+    if ((kind != lb::KIND_S8 && kind != lb::KIND_LINEAR && !s4) || cu <= 0) return 0;
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 256) >= cu) return 0;
     const int64_t wide = tiles(256, 192), tall = tiles(192, 256);
@@ -122,10 +118,10 @@ int narrow_tile_of(int kind, int64_t M, int64_t N, int64_t *count)
     return 0;
 }
 
-int narrow_w4_tile(int kind, int variant, int64_t M, int64_t N)
+int narrow_w4_tile(int kind, int variant, int64_t M, int64_t N, int cu)
 {
     int64_t count = 0;
-    const int t = variant == 6 ? narrow_tile_of(kind, M, N, &count) : 0;
+    const int t = variant == 6 ? narrow_tile_of(kind, M, N, cu, &count) : 0;
     return t ? t : variant;
 }
 
@@ -138,13 +134,11 @@ int narrow_w4_tile(int kind, int variant, int64_t M, int64_t N)
 // fewer tiles the selector's choice was faster (1.01-1.32x).  The int8 selector
 // already chose variant 6 on every shape above that fill.  An automatic choice
 // (not one fixed by LB_AUTO_VARIANT) is therefore replaced by variant 6 there.
-int prefer_full_narrow_round(int kind, int variant, int64_t M, int64_t N)
+int prefer_full_narrow_round(int kind, int variant, int64_t M, int64_t N, int cu)
 {
-    if (variant == 6 || auto_override() >= 0) return variant;
-    int cu = 0;
-    if (lb::device_cu_count(&cu) != LB_OK || cu <= 0) return variant;
+    if (variant == 6 || auto_override() >= 0 || cu <= 0) return variant;
     int64_t count = 0;
-    if (narrow_tile_of(kind, M, N, &count) && 8 * count >= 7 * (int64_t)cu) return 6;
+    if (narrow_tile_of(kind, M, N, cu, &count) && 8 * count >= 7 * (int64_t)cu) return 6;
     return variant;
 }
 
@@ -166,13 +160,12 @@ int prefer_full_narrow_round(int kind, int variant, int64_t M, int64_t N)
 // faster, 1-bit 64 x 64 x 32768 4.9x; the model declines 64 x 4096 x 4096 and
 // 1-bit 4096 x 64 x 8192, where bands lost 9% and 47%).  Returns S (1: no
 // split) and the band length in bytes.
-int plan_ksplit(int kind, int variant, int64_t M, int64_t N, int64_t kb, int64_t *band)
+int plan_ksplit(int kind, int variant, int64_t M, int64_t N, int64_t kb, int cu, int64_t *band)
 {
     *band = kb;
-    if (kind == lb::KIND_LINEAR) return 1;  // the dequantisation needs the whole sum
-    int bm = 0, bn = 0, bk = 0, st = 0, cu = 0;
+    if (kind == lb::KIND_LINEAR || cu <= 0) return 1;  // the dequantisation needs the whole sum
+    int bm = 0, bn = 0, bk = 0, st = 0;
     if (lb::mfma_variant_info(kind, variant, &bm, &bn, &bk, &st) != 0) return 1;
-    if (lb::device_cu_count(&cu) != LB_OK || cu <= 0) return 1;
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     if (4 * tiles > cu) return 1;
     const int per_byte = kind == lb::KIND_S8 ? 1 : kind == lb::KIND_S4 ? 2 : 8;
@@ -238,28 +231,32 @@ struct Plan {
     bool zero;
 };
 
-Plan make_plan(int kind, int dtype, int variant, int64_t M, int64_t N, int64_t K, int64_t kb)
+// cu: the CU count to plan for; <= 0 asks the current device (when the plan
+// needs it), and a failed query plans as with no CU information (no splits,
+// bands or narrow tiles; the selection falls back to the default variant).
+Plan make_plan(int kind, int dtype, int variant, int64_t M, int64_t N, int64_t K, int64_t kb, int cu)
 {
     Plan p{{{0, M, 0, N, variant}, {0, 0, 0, 0, 0}}, 1, kb, false};
     const bool b1 = kind == lb::KIND_B1 || kind == lb::KIND_B1F4;
+    if (variant == LB_AUTO && cu <= 0 && lb::device_cu_count(&cu) != LB_OK) cu = 0;
     if (b1 && kb > b1_pass_bytes(kind)) {
         // Long 1-bit K: bands are required for exactness (see b1_pass_bytes).
         p.band = b1_band_bytes(kind, kb);
         if (variant == LB_AUTO) {
             // An automatic choice may cut K finer still (few tiles, see below).
-            variant = resolve(dtype, LB_AUTO, M, N, K);
+            variant = resolve(dtype, LB_AUTO, M, N, K, cu);
             int64_t finer = kb;
-            if (plan_ksplit(kind, variant, M, N, kb, &finer) > 1 && finer < p.band) p.band = finer;
+            if (plan_ksplit(kind, variant, M, N, kb, cu, &finer) > 1 && finer < p.band) p.band = finer;
         }
         p.zero = true;
         p.parts[0].variant = variant;
     } else if (variant == LB_AUTO) {
-        const int v = prefer_full_narrow_round(kind, resolve(dtype, LB_AUTO, M, N, K), M, N);
-        p.np = plan_parts(dtype, v, M, N, K, p.parts);
-        if (p.np == 1 && plan_ksplit(kind, v, M, N, kb, &p.band) > 1)
+        const int v = prefer_full_narrow_round(kind, resolve(dtype, LB_AUTO, M, N, K, cu), M, N, cu);
+        p.np = plan_parts(dtype, v, M, N, K, cu, p.parts);
+        if (p.np == 1 && plan_ksplit(kind, v, M, N, kb, cu, &p.band) > 1)
             p.zero = true;
         else if (p.np == 1)
-            p.parts[0].variant = narrow_w4_tile(kind, v, M, N);
+            p.parts[0].variant = narrow_w4_tile(kind, v, M, N, cu);
     }
     return p;
 }
@@ -268,7 +265,7 @@ int run_gemm(int kind, int dtype, int variant, const void *A, const void *B, voi
              size_t out_elem, const float *sx, const float *sw, int64_t M, int64_t N, int64_t K,
              int64_t kb, void *stream)
 {
-    const Plan p = make_plan(kind, dtype, variant, M, N, K, kb);
+    const Plan p = make_plan(kind, dtype, variant, M, N, K, kb, 0);
     if (p.zero) {
         const hipError_t z = lb::launch_zero_i32((int32_t *)out, M * N, (hipStream_t)stream);
         if (z != hipSuccess) return LB_ERR_HIP;
@@ -312,8 +309,8 @@ int lb_gemm_b1(const uint32_t *A, const uint32_t *B, int32_t *C, int64_t M, int6
     return run_gemm(b1_kind(), LB_B1, variant, A, B, C, 4, nullptr, nullptr, M, N, K, K / 8, stream);
 }
 
-int lb_auto_plan(int op, int64_t M, int64_t N, int64_t K, int *launches, int *tile_m, int *tile_n,
-                 int *k_bands)
+int lb_auto_plan(int op, int64_t M, int64_t N, int64_t K, int cu_count, int *launches, int *tile_m,
+                 int *tile_n, int *k_bands)
 {
     if (M <= 0 || N <= 0 || K <= 0) return LB_ERR_SHAPE;
     int kind, dtype = op;
@@ -326,7 +323,7 @@ int lb_auto_plan(int op, int64_t M, int64_t N, int64_t K, int *launches, int *ti
     default: return LB_ERR_VARIANT;
     }
     if (kb <= 0) return LB_ERR_SHAPE;
-    const Plan p = make_plan(kind, dtype, LB_AUTO, M, N, K, kb);
+    const Plan p = make_plan(kind, dtype, LB_AUTO, M, N, K, kb, cu_count);
     int bm = 0, bn = 0, bk = 0, st = 0;
     if (lb::mfma_variant_info(kind, p.parts[0].variant, &bm, &bn, &bk, &st) != 0) return LB_ERR_VARIANT;
     if (launches) *launches = p.np;

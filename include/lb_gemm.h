@@ -198,21 +198,23 @@ int lb_conv2d_s4(const uint8_t *X, const uint8_t *F, int32_t *Y, int64_t N,
 int lb_select_variant(int dtype, int64_t M, int64_t N, int64_t K, int cu_count,
                       int *best, int *second);
 
-/* The launches an LB_AUTO call makes for a shape on the current HIP device,
- * without launching anything (host-only; for tests and tuning).  op: LB_S8,
- * LB_S4 or LB_B1 for the GEMMs, LB_PLAN_LINEAR for the int8 linear layer; M, N,
- * K as for that call.  Writes, through any non-NULL pointer: launches (1, or 2
- * for the two-launch split), tile_m x tile_n (the workgroup tile of the first
- * launch: a variant's tile, or 256 x 192 / 192 x 256, the four-wave kernel's
- * narrower tiles that an automatic choice of variant 6 takes for the int8
- * and int4 GEMMs and the linear layer when its 256x256 grid would fill less
- * than one round of the CUs and the narrower grid still fits in one), and k_bands (K
- * bands of a single launch; 1: none).  Returns LB_ERR_SHAPE for a
- * non-positive size (or K below one byte of the type), LB_ERR_VARIANT for an
- * unknown op. */
+/* The launches an LB_AUTO call makes for a shape, without launching anything
+ * (host-only; for tests and tuning).  op: LB_S8, LB_S4 or LB_B1 for the GEMMs,
+ * LB_PLAN_LINEAR for the int8 linear layer; M, N, K as for that call.
+ * cu_count: compute units to plan for; <= 0 asks the current HIP device (if
+ * none answers, the plan is the one a call would make without that
+ * information: the default variant, no splits, bands or narrow tiles).
+ * Writes, through any non-NULL pointer: launches (1, or 2 for the two-launch
+ * split), tile_m x tile_n (the workgroup tile of the first launch: a
+ * variant's tile, or 256 x 192 / 192 x 256, the four-wave kernel's narrower
+ * tiles that an automatic choice of variant 6 takes when its 256x256 grid
+ * would fill less than one round of the CUs and the narrower grid still fits
+ * in one), and k_bands (K bands of a single launch; 1: none).  Returns
+ * LB_ERR_SHAPE for a non-positive size (or K below one byte of the type),
+ * LB_ERR_VARIANT for an unknown op. */
 #define LB_PLAN_LINEAR 3
-int lb_auto_plan(int op, int64_t M, int64_t N, int64_t K, int *launches, int *tile_m,
-                 int *tile_n, int *k_bands);
+int lb_auto_plan(int op, int64_t M, int64_t N, int64_t K, int cu_count, int *launches,
+                 int *tile_m, int *tile_n, int *k_bands);
 
 /* Hash of the source files this library was built from (16 hex digits, static
  * storage; never NULL).  The build stamps it in, so that a caller can check a

@@ -161,12 +161,12 @@ def test_auto_plan_argument_checks(lib):
     the device anything (the launches it reports are checked on the GPU)."""
     out = [ctypes.c_int(0) for _ in range(4)]
     refs = [ctypes.byref(v) for v in out]
-    assert lib.lb_auto_plan(4, 64, 64, 64, *refs) == lb.LB_ERR_VARIANT
-    assert lib.lb_auto_plan(-1, 64, 64, 64, *refs) == lb.LB_ERR_VARIANT
+    assert lib.lb_auto_plan(4, 64, 64, 64, 256, *refs) == lb.LB_ERR_VARIANT
+    assert lib.lb_auto_plan(-1, 64, 64, 64, 256, *refs) == lb.LB_ERR_VARIANT
     for op in (lb.LB_S8, lb.LB_S4, lb.LB_B1, lb.LB_PLAN_LINEAR):
-        assert lib.lb_auto_plan(op, 0, 64, 64, *refs) == lb.LB_ERR_SHAPE
-        assert lib.lb_auto_plan(op, 64, -1, 64, *refs) == lb.LB_ERR_SHAPE
-        assert lib.lb_auto_plan(op, 64, 64, 0, *refs) == lb.LB_ERR_SHAPE
+        assert lib.lb_auto_plan(op, 0, 64, 64, 256, *refs) == lb.LB_ERR_SHAPE
+        assert lib.lb_auto_plan(op, 64, -1, 64, 256, *refs) == lb.LB_ERR_SHAPE
+        assert lib.lb_auto_plan(op, 64, 64, 0, 256, *refs) == lb.LB_ERR_SHAPE
     # K below one byte of a packed type
-    assert lib.lb_auto_plan(lb.LB_S4, 64, 64, 1, *refs) == lb.LB_ERR_SHAPE
-    assert lib.lb_auto_plan(lb.LB_B1, 64, 64, 7, *refs) == lb.LB_ERR_SHAPE
+    assert lib.lb_auto_plan(lb.LB_S4, 64, 64, 1, 256, *refs) == lb.LB_ERR_SHAPE
+    assert lib.lb_auto_plan(lb.LB_B1, 64, 64, 7, 256, *refs) == lb.LB_ERR_SHAPE
