@@ -166,7 +166,18 @@ def conv_step(name, torch, lb):
         if Co <= 64:
             return 0
         return lb.lb_select_variant(lb.LB_S8 if dtype == "s8" else lb.LB_S4, M, Co, K, 0)[0]
+
+    def auto_tile():
+        # the tile an automatic call runs: for at most 64 output channels with a
+        # window of several taps and at most 1024 bytes, the 64x64 tile with
+        # two 64-byte stages; else the selected variant's tile
+        kb = Kh * Kw * (C if dtype == "s8" else C // 2)
+        if Co <= 64 and kb <= 1024 and Kh * Kw > 1:
+            return "64x64, two 64-byte stages"
+        info = lb.lb_variant_info(lb.LB_S8 if dtype == "s8" else lb.LB_S4, selected())
+        return f"{info['tile_m']}x{info['tile_n']}, {info['stages']} stages (variant {selected()})"
     run.selected = selected
+    run.auto_tile = auto_tile
     nbytes = X.numel() + F.numel() + 4 * Y.numel()
     return run, (M, Co, K), nbytes
 
@@ -183,7 +194,7 @@ def conv_roofline(ops, nbytes, t):
 
 
 def measure_conv(name, torch, lb):
-    """Convolution layer: kernel time (HIP-graph replay), its roofline, and the
+    """Convolution layer: kernel time of the automatic call (HIP-graph replay), its roofline, and the
     GEMM of the same M, N, K on dense operands (the cost of gathering windows)."""
     from bit_integer_gemm_amd.sweep import time_calls
     dtype = CONV_LAYERS[name][0]
@@ -192,13 +203,14 @@ def measure_conv(name, torch, lb):
     ops_ = make_operands(dtype, M, N, K, (7001, 7002), torch)
     out = out_buffer(dtype, M, N, torch)
     grun, _ = step_fn(dtype, ops_, out, lb)
-    time_calls(lambda: run(sel), torch, target_ms=10.0, groups=1)   # see measure()
+    time_calls(lambda: run(), torch, target_ms=10.0, groups=1)   # see measure()
     t = tg = float("inf")
     for _ in range(2):
-        t = min(t, time_calls(lambda: run(sel), torch, target_ms=30.0, groups=5)[0])
+        t = min(t, time_calls(lambda: run(), torch, target_ms=30.0, groups=5)[0])
         tg = min(tg, time_calls(lambda: grun(sel), torch, target_ms=30.0, groups=5)[0])
     ops = 2.0 * M * N * K
-    return {"gemm_shape": [M, N, K], "variant": sel, "us_per_call": round(t * 1e6, 2),
+    return {"gemm_shape": [M, N, K], "variant": sel, "automatic_tile": run.auto_tile(),
+            "us_per_call": round(t * 1e6, 2),
             "tops": round(ops / t / 1e12, 2), "roofline": conv_roofline(ops, nbytes, t),
             "algorithmic_bytes": nbytes, "same_shape_gemm_us": round(tg * 1e6, 2),
             "conv_over_gemm_time": round(t / tg, 4)}

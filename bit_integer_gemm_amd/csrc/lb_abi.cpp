@@ -379,10 +379,19 @@ int conv_entry(int kind, int dtype, const void *X, const void *F, int32_t *Y, in
     // 0-29% over the GEMM's choice (int8 3x3 over 32 x 56x56x64 -> 64: 16.2
     // against 19.6 us; a 7x7 stride-2 stem: 72.9 against 89.1 us), the window
     // gather of a wider tile costing more than its column reuse saves; with 96
-    // or 128 the GEMM's choice was within 3.4% of the best.
+    // or 128 the GEMM's choice was within 3.4% of the best.  With windows of
+    // several taps and at most 1024 bytes the same 64x64 tile runs with two
+    // 64-byte stages instead (16 KiB of LDS: eight workgroups per CU against
+    // five), since such layers are many short workgroups and what pays is how
+    // many a CU holds.  Measured in one process against variant 0 (identical
+    // results): int4 1.12-1.18x (7x7 stride-2 stem over 32 x 224x224x32 79.8
+    // against 89.4 us, 3x3 over 8 x 112x112x32 12.1 against 14.3 us); int8
+    // 0.99-1.12x (3x3 over 8 x 112x112x32 12.7 against 14.2 us, the stem
+    // 73.4 against 72.9 us); a 1x1 layer lost 4% and windows of 1152 bytes
+    // (3x3 over 28x28x128) 18% in an earlier build, so those keep variant 0.
     int v = variant;
     if (v == LB_AUTO && (v = auto_override()) < 0) {
-        if (Co <= 64) v = 0;
+        if (Co <= 64) v = (Kb <= 1024 && Kh * Kw > 1) ? lb::CONV_64x64_K64 : 0;
         else if (lb::select_from_table(dtype, M, Co, K, 0, &v, nullptr) != LB_OK) v = LB_DEFAULT_VARIANT;
     }
     lb::ConvGeom g;

@@ -15,6 +15,9 @@ enum { KIND_S8 = 0, KIND_S4 = 1, KIND_LINEAR = 2, KIND_B1 = 3, KIND_B1F4 = 4 };
 // caller): the four-wave kernel on 256x192 tiles (int8, int4 and 1-bit FP4-
 // route GEMMs, linear layer) and on 192x256 tiles (int8 GEMM, linear layer).
 enum { W4_256x192 = 16, W4_192x256 = 17 };
+// Internal tile code of the convolutions: a 64x64 tile with two 64-byte
+// stages (16 KiB of LDS, up to eight workgroups per CU).
+enum { CONV_64x64_K64 = 18 };
 
 // int8 MFMA family (int8 GEMM, packed-int4 GEMM, int8 linear layer, and the
 // 1-bit GEMM on weighted bit planes).  Kb is the row length of A and B in

@@ -1305,6 +1305,7 @@ static hipError_t launch_w4(const void *A, const void *B, void *out, const float
 using S2 = MfmaCfg<64, 64, 128, 2, 2, 2>;     // 32 KiB
 using S3 = MfmaCfg<64, 64, 128, 2, 2, 3>;     // 48 KiB
 using S4 = MfmaCfg<64, 64, 128, 2, 2, 4>;     // 64 KiB
+using SK64 = MfmaCfg<64, 64, 64, 2, 2, 2>;    // 16 KiB, convolutions with a short K
 // The 2-stage medium tile runs 8 waves of 32x64 (two workgroups per CU): 3-16%
 // faster than 4 waves of 64x64 on most shapes that choose it (4% slower at
 // 1024 x 1024 x 4096); the 3- and 4-stage medium tiles lose with 8 waves and
@@ -1387,6 +1388,10 @@ static hipError_t dispatch(int variant, const void *A, const void *B, void *out,
             return launch_one<std::conditional_t<b1 || (KIND == KIND_S4 && !CONV), L2W8, L2W16>, KIND, CONV>(
                 A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
     case 7: return launch_one<L3W8, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+    case CONV_64x64_K64:
+        // internal: the convolutions' small tile with 64-byte stages
+        if constexpr (CONV) return launch_one<SK64, KIND, CONV>(A, B, out, sx, sw, M, N, Kb, ldo, ksplit, g, s);
+        return hipErrorInvalidValue;
     case W4_256x192:
     case W4_192x256:
         // internal: the narrower four-wave tiles, int8 GEMM and linear layer
@@ -1468,6 +1473,7 @@ int mfma_variant_info(int kind, int variant, int *bm, int *bn, int *bk_bytes, in
     case 7: info_one<L3W8>(bm, bn, bk_bytes, stages); return 0;
     case 8: info_one<L4W16>(bm, bn, bk_bytes, stages); return 0;
     case W4_256x192: *bm = 256; *bn = 192; *bk_bytes = 128; *stages = 2; return 0;
+    case CONV_64x64_K64: info_one<SK64>(bm, bn, bk_bytes, stages); return 0;
     case W4_192x256: *bm = 192; *bn = 256; *bk_bytes = 128; *stages = 2; return 0;
     default: return -1;
     }

@@ -158,7 +158,9 @@ int lb_gemm_s8_linear(const int8_t *X, const int8_t *W, const float *sx,
  * It runs as a GEMM with M = N*Ho*Wo, N = Co, K = Kh*Kw*C whose A rows (the
  * page's windows) are read straight from X: no window or column buffer is
  * allocated.  LB_AUTO picks the variant the GEMM of that shape would get, or
- * the small 2-stage tile (variant 0) when Co <= 64.
+ * when Co <= 64 the small 64x64 tile: with two 64-byte stages (an internal
+ * tile, up to eight workgroups per CU) when the filter has more than one tap
+ * and a window holds at most 1024 bytes, else the 2-stage tile of variant 0.
  * C must be a multiple of LB_CONV_S8_C_ALIGN (int8) or LB_CONV_S4_C_ALIGN
  * (int4, packed two per byte along C, even c in the low nibble, for X and F
  * alike): 16 bytes per pixel or a multiple, else LB_ERR_ALIGN.  (A layer with

@@ -212,10 +212,11 @@ def test_conv_graph_capture_replays_match_eager():
 
 
 def test_conv_extreme_values():
-    """All -128 operands with padding: every output is 16384*C times its in-image tap count."""
+    """All -128 operands with padding: every output is 16384*C times its in-image
+    tap count (the automatic choice here is the 64x64 tile with 64-byte stages)."""
     N, H, W, C, Co, Kh, Kw, st, pd = 1, 6, 7, 64, 20, 3, 3, (1, 2), (1, 1)
     x = np.full((N, H, W, C), -128, np.int8)
     f = np.full((Co, Kh, Kw, C), -128, np.int8)
     want = oracle.conv2d_s8(x, f, st, pd)
-    for v in range(lb.LB_NUM_VARIANTS):
+    for v in [lb.LB_AUTO] + list(range(lb.LB_NUM_VARIANTS)):
         np.testing.assert_array_equal(run_conv("s8", x, f, st, pd, v), want)
